@@ -1,0 +1,475 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the fused layer-boundary ops.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h).  Written for a reader checking it
+ * against the pages by eye: one loop per definition, double precision, no
+ * blocking, no fusion, no reordering beyond what each definition states.
+ *
+ * Parity pins: every function here is pinned by the CPU tests (closed forms,
+ * invariants, brute force and library routines); none is "parity unpinned".
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* Number formats                                                      */
+/* ------------------------------------------------------------------ */
+
+/* Round v to a binary format with p significand bits (hidden bit
+ * included) whose smallest normal exponent is emin, ties to even.  Below
+ * 2^emin the quantum stays 2^(emin-p+1) (gradual underflow).  No overflow
+ * handling here; the callers decide what happens above the format's max. */
+static double round_to_format(double v, int p, int emin)
+{
+    if (v == 0.0 || !isfinite(v))
+        return v;
+    int e;
+    frexp(fabs(v), &e);             /* |v| = f * 2^e, f in [0.5, 1) */
+    int lead = e - 1;               /* exponent of the leading bit */
+    if (lead < emin)
+        lead = emin;
+    double quantum = ldexp(1.0, lead - (p - 1));
+    /* v / quantum is exact (power-of-two scaling); nearbyint rounds to
+     * nearest with ties to even under the default rounding mode. */
+    return nearbyint(v / quantum) * quantum;
+}
+
+/* Bits of an already-rounded finite value r in a format with the given
+ * significand bits p, exponent bias and smallest normal exponent emin. */
+static uint32_t pack_bits(double r, int p, int bias, int emin, int ebits)
+{
+    uint32_t sign = signbit(r) ? 1u : 0u;
+    double a = fabs(r);
+    uint32_t E, M;
+    if (a < ldexp(1.0, emin)) {                 /* subnormal or zero */
+        E = 0;
+        M = (uint32_t)(a / ldexp(1.0, emin - (p - 1)));
+    } else {
+        int e;
+        frexp(a, &e);
+        int lead = e - 1;
+        E = (uint32_t)(lead + bias);
+        M = (uint32_t)(ldexp(a, (p - 1) - lead) - ldexp(1.0, p - 1));
+    }
+    return (sign << (ebits + p - 1)) | (E << (p - 1)) | M;
+}
+
+double or_f16_decode(uint16_t bits)
+{
+    int s = bits >> 15, e = (bits >> 10) & 0x1F, m = bits & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return s ? -v : v;
+}
+
+double or_bf16_decode(uint16_t bits)
+{
+    int s = bits >> 15, e = (bits >> 7) & 0xFF, m = bits & 0x7F;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -133);
+    else if (e == 255)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + m), e - 134);
+    return s ? -v : v;
+}
+
+uint16_t or_f16_encode(double v)
+{
+    if (isnan(v))
+        return 0x7E00;
+    double r = round_to_format(v, 11, -14);
+    if (fabs(r) > 65504.0)
+        return (uint16_t)((signbit(r) ? 0x8000 : 0) | 0x7C00);
+    return (uint16_t)pack_bits(r, 11, 15, -14, 5);
+}
+
+uint16_t or_bf16_encode(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    double r = round_to_format(v, 8, -126);
+    if (fabs(r) > ldexp(255.0, 120))            /* (2 - 2^-7) * 2^127 */
+        return (uint16_t)((signbit(r) ? 0x8000 : 0) | 0x7F80);
+    return (uint16_t)pack_bits(r, 8, 127, -126, 8);
+}
+
+/* OCP 8-bit E4M3 ("fn"): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits,
+ * subnormals m * 2^-9, no infinities, S.1111.111 is NaN, largest finite
+ * value 448 (S.1111.110). */
+double or_e4m3_decode(uint8_t code)
+{
+    int s = code >> 7, e = (code >> 3) & 0xF, m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+/* Saturating encoder: NaN -> 0x7F, otherwise clamp to [-448, 448] and round
+ * to nearest, ties to even.  The sign is kept, so a negative value that
+ * rounds to zero gives 0x80. */
+uint8_t or_e4m3_encode(double v)
+{
+    if (isnan(v))
+        return 0x7F;
+    if (v > 448.0)
+        v = 448.0;
+    if (v < -448.0)
+        v = -448.0;
+    double r = round_to_format(v, 4, -6);
+    return (uint8_t)pack_bits(r, 4, 7, -6, 4);
+}
+
+float or_f32_round(double v)
+{
+    return (float)v;                 /* C conversion: round to nearest even */
+}
+
+/* Array forms of the encoders (used by the tests to sweep many values). */
+void or_e4m3_encode_n(const double* v, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = or_e4m3_encode(v[i]);
+}
+
+void or_f16_encode_n(const double* v, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = or_f16_encode(v[i]);
+}
+
+void or_bf16_encode_n(const double* v, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = or_bf16_encode(v[i]);
+}
+
+static double dec16(uint16_t bits, int dtype)
+{
+    return dtype == OR_BF16 ? or_bf16_decode(bits) : or_f16_decode(bits);
+}
+
+static uint16_t enc16(double v, int dtype)
+{
+    return dtype == OR_BF16 ? or_bf16_encode(v) : or_f16_encode(v);
+}
+
+/* ------------------------------------------------------------------ */
+/* Building blocks                                                     */
+/* ------------------------------------------------------------------ */
+
+/* RMSNorm scale [FR section 二, step 1]: rstd = 1 / sqrt(mean(v^2) + eps),
+ * eps inside the square root, mean over the n normalised elements. */
+double or_rms_rstd(const double* v, int64_t n, double eps)
+{
+    double ss = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        ss += v[j] * v[j];
+    return 1.0 / sqrt(ss / (double)n + eps);
+}
+
+/* RMSNorm with the three weight conventions [FR section 二 2.1 and section
+ * 三]: none (the "_noweight" kernel, weight already folded into the next
+ * GEMM), y*w, or y*(1+w). */
+void or_rmsnorm(const double* v, const double* w, int wmode, int64_t n,
+                double eps, double* y)
+{
+    double rstd = or_rms_rstd(v, n, eps);
+    for (int64_t j = 0; j < n; ++j) {
+        double W = 1.0;
+        if (wmode == OR_W_MUL)
+            W = w[j];
+        else if (wmode == OR_W_ONE_PLUS)
+            W = 1.0 + w[j];
+        y[j] = v[j] * rstd * W;
+    }
+}
+
+/* Adaptive RMSNorm modulation [FR section 三]: normalise, then scale by
+ * (1 + scale) and add shift; no learned weight. */
+void or_adarms(const double* h, const double* scale, const double* shift,
+               int64_t n, double eps, double* y)
+{
+    double rstd = or_rms_rstd(h, n, eps);
+    for (int64_t j = 0; j < n; ++j)
+        y[j] = h[j] * rstd * (1.0 + scale[j]) + shift[j];
+}
+
+/* Rotary position embedding, in place on one head of D elements [FR
+ * section 二 2.2].  Pair i (0 <= i < D/2) turns by pos * theta^(-2i/D).
+ * ROPE_HALF pairs element i with element i + D/2; ROPE_INTERLEAVED pairs
+ * element 2i with element 2i+1.  In each pair (a, b) -> (a cos - b sin,
+ * b cos + a sin). */
+void or_rope(double* v, int64_t D, int64_t pos, double theta, int style)
+{
+    int64_t half = D / 2;
+    for (int64_t i = 0; i < half; ++i) {
+        double inv_freq = pow(theta, -(2.0 * (double)i) / (double)D);
+        double ang = (double)pos * inv_freq;
+        double c = cos(ang), s = sin(ang);
+        int64_t ia = style == OR_ROPE_INTERLEAVED ? 2 * i : i;
+        int64_t ib = style == OR_ROPE_INTERLEAVED ? 2 * i + 1 : i + half;
+        double a = v[ia], b = v[ib];
+        v[ia] = a * c - b * s;
+        v[ib] = b * c + a * s;
+    }
+}
+
+/* Gate activations: SiLU (SwiGLU) [SM89 Phase 2], GELU with the tanh
+ * approximation (GeGLU) [FR section 二 table, steps 8-10] and squared ReLU
+ * [FP, third technique]. */
+double or_act(double g, int act)
+{
+    switch (act) {
+    case OR_ACT_SWIGLU:
+        return g / (1.0 + exp(-g));
+    case OR_ACT_GEGLU_TANH: {
+        const double k = sqrt(2.0 / acos(-1.0));   /* sqrt(2/pi) */
+        return 0.5 * g * (1.0 + tanh(k * (g + 0.044715 * g * g * g)));
+    }
+    case OR_ACT_SQRELU:
+        return g > 0.0 ? g * g : 0.0;
+    default:
+        return NAN;
+    }
+}
+
+/* Static quantisation ("_static": the activation scale is a fixed
+ * constant, [FR section 六]): code = E(y * mult). */
+void or_quant_static(const double* y, int64_t n, double mult, uint8_t* q)
+{
+    for (int64_t j = 0; j < n; ++j)
+        q[j] = or_e4m3_encode(y[j] * mult);
+}
+
+/* Dynamic quantisation of one group (a token row, or one block of 128
+ * outputs of a row) [SM89 Phase 2]: the dequant scale is the group's
+ * largest magnitude over 448 (floored so that an all-zero group stays
+ * finite), stored as fp32; code = E(y / scale). */
+float or_quant_dynamic(const double* y, int64_t n, uint8_t* q)
+{
+    const double floor_amax = (double)1e-10f;
+    double amax = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        if (fabs(y[j]) > amax)
+            amax = fabs(y[j]);
+    if (amax < floor_amax)
+        amax = floor_amax;
+    float s = or_f32_round(amax / 448.0);
+    for (int64_t j = 0; j < n; ++j)
+        q[j] = or_e4m3_encode(y[j] / (double)s);
+    return s;
+}
+
+/* Paged KV-cache slot of a token position [FP, paged cache]: page
+ * page_table[pos / page_size], offset pos % page_size.  -1 when the
+ * position, the table entry or the page is out of range. */
+int64_t or_kv_slot(int64_t pos, const int32_t* page_table, int32_t table_len,
+                   int32_t page_size, int32_t num_pages)
+{
+    if (pos < 0)
+        return -1;
+    int64_t idx = pos / page_size;
+    if (idx >= table_len)
+        return -1;
+    int64_t page = page_table[idx];
+    if (page < 0 || page >= num_pages)
+        return -1;
+    return page * page_size + pos % page_size;
+}
+
+/* ------------------------------------------------------------------ */
+/* Fused ops                                                           */
+/* ------------------------------------------------------------------ */
+
+/* Residual add + RMSNorm + FP8 [FR section 二 table step 1, 2.1]:
+ *   residual_out = round(x + residual)
+ *   y = RMSNorm(residual_out) with the chosen weight convention
+ *   STATIC: code = E(y * static_scale);
+ *   TOKEN:  scale_t = amax_t / 448, code = E(y / scale_t). */
+int oracle_resid_rmsnorm_fp8(const uint16_t* x, const uint16_t* residual,
+                             uint16_t* residual_out, const uint16_t* weight,
+                             int wmode, float eps, uint8_t* out_fp8, int qmode,
+                             float static_scale, float* out_scales,
+                             int64_t T, int64_t H, int dtype)
+{
+    double* ro = malloc(sizeof(double) * (size_t)H);
+    double* w = malloc(sizeof(double) * (size_t)H);
+    double* y = malloc(sizeof(double) * (size_t)H);
+    if (!ro || !w || !y) {
+        free(ro); free(w); free(y);
+        return -1;
+    }
+    for (int64_t j = 0; j < H; ++j)
+        w[j] = (wmode != OR_W_NONE) ? dec16(weight[j], dtype) : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* xr = x + t * H;
+        const uint16_t* rr = residual + t * H;
+        uint16_t* orow = residual_out + t * H;
+        for (int64_t j = 0; j < H; ++j) {
+            uint16_t b = enc16(dec16(xr[j], dtype) + dec16(rr[j], dtype), dtype);
+            orow[j] = b;
+            ro[j] = dec16(b, dtype);        /* the norm reads the stored value */
+        }
+        or_rmsnorm(ro, w, wmode, H, (double)eps, y);
+        if (qmode == OR_Q_STATIC)
+            or_quant_static(y, H, (double)static_scale, out_fp8 + t * H);
+        else
+            out_scales[t] = or_quant_dynamic(y, H, out_fp8 + t * H);
+    }
+    free(ro); free(w); free(y);
+    return 0;
+}
+
+/* Gate multiply + residual + adaptive RMSNorm + FP8 [FR section 三]:
+ *   residual_out = round(residual + gate * x)
+ *   y = RMSNorm(residual_out) * (1 + ada_scale) + ada_shift
+ *   quantised as in the op above. */
+int oracle_adarms_gate_res_fp8(const uint16_t* x, const uint16_t* gate,
+                               const uint16_t* residual, uint16_t* residual_out,
+                               const uint16_t* ada_scale, const uint16_t* ada_shift,
+                               float eps, uint8_t* out_fp8, int qmode,
+                               float static_scale, float* out_scales,
+                               int64_t T, int64_t H, int dtype)
+{
+    double* ro = malloc(sizeof(double) * (size_t)H);
+    double* sc = malloc(sizeof(double) * (size_t)H);
+    double* sh = malloc(sizeof(double) * (size_t)H);
+    double* y = malloc(sizeof(double) * (size_t)H);
+    if (!ro || !sc || !sh || !y) {
+        free(ro); free(sc); free(sh); free(y);
+        return -1;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t o = t * H;
+        for (int64_t j = 0; j < H; ++j) {
+            double h = dec16(residual[o + j], dtype)
+                     + dec16(gate[o + j], dtype) * dec16(x[o + j], dtype);
+            uint16_t b = enc16(h, dtype);
+            residual_out[o + j] = b;
+            ro[j] = dec16(b, dtype);
+            sc[j] = dec16(ada_scale[o + j], dtype);
+            sh[j] = dec16(ada_shift[o + j], dtype);
+        }
+        or_adarms(ro, sc, sh, H, (double)eps, y);
+        if (qmode == OR_Q_STATIC)
+            or_quant_static(y, H, (double)static_scale, out_fp8 + o);
+        else
+            out_scales[t] = or_quant_dynamic(y, H, out_fp8 + o);
+    }
+    free(ro); free(sc); free(sh); free(y);
+    return 0;
+}
+
+/* Packed QKV split + per-head Q/K RMSNorm + RoPE + KV-cache write [FR
+ * section 二 table step 3 and 2.2; FP paged cache]:
+ *   row t of qkv = [Q heads (Hq*D) | K heads (Hkv*D) | V heads (Hkv*D)]
+ *   Q, K heads: optional RMSNorm over D with a weight shared by all heads
+ *   (skipped when the weight pointer is NULL), then RoPE at positions[t],
+ *   then one rounding to the storage type.  Q goes to q_out[t, h, :]; K to
+ *   k_cache[slot, g, :]; V is copied bit for bit to v_cache[slot, g, :].
+ *   An out-of-range slot skips that token's K/V writes and sets bit 0 of
+ *   *err_flag (when err_flag is given). */
+int oracle_qkv_normrope_kvwrite(const uint16_t* qkv, const uint16_t* q_norm_w,
+                                const uint16_t* k_norm_w, float eps,
+                                const int32_t* positions, float rope_theta,
+                                int rope_style, uint16_t* q_out,
+                                uint16_t* k_cache, uint16_t* v_cache,
+                                const int32_t* page_table, int32_t page_table_len,
+                                int32_t page_size, int32_t num_pages,
+                                int32_t* err_flag, int64_t T, int32_t Hq,
+                                int32_t Hkv, int32_t D, int dtype)
+{
+    int64_t row = (int64_t)(Hq + 2 * Hkv) * D;
+    double* v = malloc(sizeof(double) * (size_t)D);
+    double* y = malloc(sizeof(double) * (size_t)D);
+    double* qw = malloc(sizeof(double) * (size_t)D);
+    double* kw = malloc(sizeof(double) * (size_t)D);
+    if (!v || !y || !qw || !kw) {
+        free(v); free(y); free(qw); free(kw);
+        return -1;
+    }
+    for (int32_t d = 0; d < D; ++d) {
+        qw[d] = q_norm_w ? dec16(q_norm_w[d], dtype) : 1.0;
+        kw[d] = k_norm_w ? dec16(k_norm_w[d], dtype) : 1.0;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t pos = positions[t];
+        int64_t slot = or_kv_slot(pos, page_table, page_table_len, page_size,
+                                  num_pages);
+        if (slot < 0 && err_flag)
+            *err_flag |= 1;
+        for (int32_t h = 0; h < Hq + 2 * Hkv; ++h) {
+            const uint16_t* src = qkv + t * row + (int64_t)h * D;
+            if (h >= Hq + Hkv) {                      /* V: pass-through */
+                int32_t g = h - Hq - Hkv;
+                if (slot >= 0)
+                    memcpy(v_cache + (slot * Hkv + g) * D, src,
+                           sizeof(uint16_t) * (size_t)D);
+                continue;
+            }
+            int is_q = h < Hq;
+            const uint16_t* nw = is_q ? q_norm_w : k_norm_w;
+            for (int32_t d = 0; d < D; ++d)
+                v[d] = dec16(src[d], dtype);
+            if (nw) {
+                or_rmsnorm(v, is_q ? qw : kw, OR_W_MUL, D, (double)eps, y);
+                memcpy(v, y, sizeof(double) * (size_t)D);
+            }
+            or_rope(v, D, pos, (double)rope_theta, rope_style);
+            uint16_t* dst;
+            if (is_q) {
+                dst = q_out + (t * Hq + h) * D;
+            } else {
+                if (slot < 0)
+                    continue;
+                dst = k_cache + (slot * Hkv + (h - Hq)) * D;
+            }
+            for (int32_t d = 0; d < D; ++d)
+                dst[d] = enc16(v[d], dtype);
+        }
+    }
+    free(v); free(y); free(qw); free(kw);
+    return 0;
+}
+
+/* Gated activation on interleaved gate/up + per-token block-128 FP8 [SM89
+ * Phase 2; FP third technique]:
+ *   gate_up row t = [g0, u0, g1, u1, ...] (2I values)
+ *   h_j = act(g_j) * u_j, kept unrounded
+ *   for each block b of 128 consecutive outputs: scale[t, b] = amax/448,
+ *   code = E(h / scale). */
+int oracle_gated_act_fp8(const uint16_t* gate_up, int act, uint8_t* out_fp8,
+                         float* out_scales, int64_t T, int64_t I, int dtype)
+{
+    const int64_t B = 128;
+    double h[128];
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* gu = gate_up + t * 2 * I;
+        for (int64_t b = 0; b < I / B; ++b) {
+            for (int64_t k = 0; k < B; ++k) {
+                int64_t j = b * B + k;
+                double g = dec16(gu[2 * j], dtype);
+                double u = dec16(gu[2 * j + 1], dtype);
+                h[k] = or_act(g, act) * u;
+            }
+            out_scales[t * (I / B) + b] =
+                or_quant_dynamic(h, B, out_fp8 + t * I + b * B);
+        }
+    }
+    return 0;
+}
