@@ -1,0 +1,404 @@
+"""Benchmark of the fused layer-boundary kernels on one MI355X.
+
+One step = one pass of the whole hot path over one batch of 8192 tokens:
+  (a)  residual add + RMSNorm(w) + per-token FP8, hidden 4096, bf16
+  (a') gate + residual + AdaRMSNorm + static FP8, hidden 1024, fp16
+  (b)  packed QKV split + Q/K RMSNorm + RoPE + paged KV write, 32/8 heads x 128,
+       bf16, 16-token pages
+  (c)  SwiGLU on interleaved gate/up + block-128 FP8, inter 12288, bf16
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+`value` is the step's algorithmic bytes over its time (GB/s).  The line also
+carries per-op microseconds, the roofline of the dominant kernel (measured
+with HIP events on the launch stream), the 10-token decoder chain
+(18 layers x 10 steps x 2 ops) replayed as one HIP graph, and the CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_HBM_GBS = 8000.0
+T_BIG = 8192
+EPS = 1e-6
+
+
+def op_bytes():
+    """Algorithmic HBM bytes per call (each input read once, each output
+    written once; 16-bit values 2 B, FP8 1 B, fp32 scales 4 B, int32 4 B)."""
+    T = T_BIG
+    H_a, H_ada = 4096, 1024
+    Hq, Hkv, D, P = 32, 8, 128, 16
+    I = 12288
+    return {
+        # x, residual in; residual_out, fp8 out; weight; per-token scales
+        "resid_rmsnorm_fp8": T * H_a * (2 + 2 + 2 + 1) + 2 * H_a + 4 * T,
+        # x, gate, residual, scale, shift in; residual_out, fp8 out
+        "adarms_gate_res_fp8": T * H_ada * (5 * 2 + 2 + 1),
+        # qkv in; q_out + k + v out; positions; page-table entries; 2 norm weights
+        "qkv_normrope_kvwrite": 2 * T * (Hq + 2 * Hkv) * D * 2 + 4 * T
+        + 4 * (T // P) + 2 * D * 2,
+        # gate_up in; fp8 out; block scales
+        "gated_act_fp8": T * 2 * I * 2 + T * I + 4 * T * (I // 128),
+    }
+
+
+def kernel_source_hash(name):
+    with open(os.path.join(HERE, "memory_bound_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file, per_launch_bytes_key):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 PMC
+    summary, only if it was taken on the current kernel source."""
+    path = os.path.join(HERE, "profiles", "gated_act_fp8_T8192_I12288_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha256_16") != kernel_source_hash(kernel_file):
+        return None
+    return d.get(per_launch_bytes_key)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chain-replays", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the fused ops are row-independent "
+              "and run on one GPU's share of tokens; multi-GPU runs are not "
+              "part of this benchmark (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import memory_bound_amd as fr
+    from memory_bound_amd.hipgraph import HipGraph
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda()
+        return torch.from_numpy(a).cuda()
+
+    torch.cuda.init()
+    stream = torch.cuda.Stream()
+    T = T_BIG
+    t0 = time.time()
+
+    # ---- inputs (seeded, synthetic, resident in HBM) ----------------------
+    ri = workloads.resid_rmsnorm_inputs(T, 4096, workloads.BF16, 105, outliers=True)
+    A = {k: dev(v) for k, v in ri.items()}
+    A["ro"] = torch.empty_like(A["x"])
+    A["q"] = torch.empty((T, 4096), dtype=torch.uint8, device="cuda")
+    A["sc"] = torch.empty((T,), dtype=torch.float32, device="cuda")
+
+    ai = workloads.adarms_inputs(T, 1024, workloads.F16, 102)
+    Ad = {k: dev(v) for k, v in ai.items()}
+    Ad["ro"] = torch.empty_like(Ad["x"])
+    Ad["q"] = torch.empty((T, 1024), dtype=torch.uint8, device="cuda")
+
+    qi = workloads.qkv_inputs(T, 32, 8, 128, workloads.BF16, 103, page_size=16,
+                              num_pages=512)
+    B = {k: dev(v) for k, v in qi.items()}
+    B["q_out"] = torch.empty((T, 32, 128), dtype=torch.int16, device="cuda")
+    B["err"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    gi = workloads.gated_act_inputs(T, 12288, workloads.BF16, 105, outliers=True)
+    C = {"gu": dev(gi["gate_up"])}
+    C["q"] = torch.empty((T, 12288), dtype=torch.uint8, device="cuda")
+    C["sc"] = torch.empty((T, 96), dtype=torch.float32, device="cuda")
+    del ri, ai, qi, gi
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def op_a():
+        fr.fr_resid_rmsnorm_fp8(A["x"], A["residual"], A["ro"], A["weight"],
+                                fr.W_MUL, EPS, A["q"], fr.Q_TOKEN, 0.0, A["sc"],
+                                T, 4096, fr.BF16, stream=stream)
+
+    def op_ada():
+        fr.fr_adarms_gate_res_fp8(Ad["x"], Ad["gate"], Ad["residual"], Ad["ro"],
+                                  Ad["ada_scale"], Ad["ada_shift"], EPS, Ad["q"],
+                                  fr.Q_STATIC, 56.0, None, T, 1024, fr.F16,
+                                  stream=stream)
+
+    def op_b():
+        fr.fr_qkv_normrope_kvwrite(B["qkv"], B["q_norm_w"], B["k_norm_w"], EPS,
+                                   B["positions"], 1e6, fr.ROPE_HALF, B["q_out"],
+                                   B["k_cache"], B["v_cache"], B["page_table"],
+                                   512, 16, 512, B["err"], T, 32, 8, 128,
+                                   fr.BF16, stream=stream)
+
+    def op_c():
+        fr.fr_gated_act_fp8(C["gu"], fr.ACT_SWIGLU, C["q"], C["sc"], T, 12288,
+                            fr.BF16, stream=stream)
+
+    ops = [("resid_rmsnorm_fp8", op_a), ("adarms_gate_res_fp8", op_ada),
+           ("qkv_normrope_kvwrite", op_b), ("gated_act_fp8", op_c)]
+    nbytes = op_bytes()
+    step_bytes = sum(nbytes.values())
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            for _, f in ops:
+                f()
+        stream.synchronize()
+
+        # ---- timed region: K steps, events around every launch ----------
+        ev = [[(torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in ops]
+              for _ in range(args.steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(args.steps):
+            for (name, f), (e0, e1) in zip(ops, ev[k]):
+                e0.record(stream)
+                f()
+                e1.record(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    per_op = {}
+    for i, (name, _) in enumerate(ops):
+        ts = np.array([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)])
+        us = ts * 1e3
+        per_op[name] = {
+            "bytes": nbytes[name],
+            "us_mean": round(float(us.mean()), 3),
+            "us_p10": round(float(np.percentile(us, 10)), 3),
+            "us_p50": round(float(np.percentile(us, 50)), 3),
+            "us_p90": round(float(np.percentile(us, 90)), 3),
+            "GBps": round(nbytes[name] / (us.mean() * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(nbytes[name] / (us.mean() * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        }
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    dom = "gated_act_fp8"
+    dom_us = per_op[dom]["us_mean"]
+    achieved = nbytes[dom] / (dom_us * 1e-6) / 1e9
+    roofline = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / PEAK_HBM_GBS, 4),
+        "traffic": load_traffic("fr_act.hip", "hbm_bytes_per_launch"),
+        "algorithmic_bytes_per_launch": nbytes[dom],
+        "avg_launch_us": dom_us,
+    }
+
+    # ---- 10-token decoder chain: 18 layers x 10 steps, one HIP graph -----
+    chain = run_chain(torch, fr, workloads, HipGraph, dev, stream,
+                      args.chain_replays)
+
+    # ---- standalone 10-token decode-boundary calls (median of 50) --------
+    small = run_small(torch, fr, workloads, dev, stream)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    line = {
+        "metric": "achieved HBM GB/s (% of peak) per fused op; us/call at T=10 and T=8192",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "layer-boundary pass at 8192 tokens: resid+RMSNorm+FP8 "
+                        "(H=4096 bf16), AdaRMSNorm+gate+FP8 (H=1024 fp16), "
+                        "QKV norm+RoPE+paged KV (32/8x128 bf16), SwiGLU+block-128 "
+                        "FP8 (I=12288 bf16)",
+            "tokens": T,
+            "step_bytes": step_bytes,
+            "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        },
+        "per_op": per_op,
+        "roofline": roofline,
+        "chain": chain,
+        "decode_t10": small,
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_chain(torch, fr, workloads, HipGraph, dev, stream, replays):
+    ci = workloads.chain_inputs()
+    d = ci["dims"]
+    L, S, T, H = d["layers"], d["steps"], d["T"], d["H"]
+    x, qkv = dev(ci["x"]), dev(ci["qkv"])
+    gate, sc, sh = dev(ci["gate"]), dev(ci["ada_scale"]), dev(ci["ada_shift"])
+    res = torch.empty((L * S + 1, T, H), dtype=torch.int16, device="cuda")
+    res[0] = dev(ci["r0"])
+    q8 = torch.empty((L * S, T, H), dtype=torch.uint8, device="cuda")
+    q_out = torch.empty((L, T, d["Hq"], d["D"]), dtype=torch.int16, device="cuda")
+    kc, vc = dev(ci["k_cache"]), dev(ci["v_cache"])
+    pos, table = dev(ci["positions"]), dev(ci["page_table"])
+
+    def run():
+        n = 0
+        for _ in range(S):
+            for l in range(L):
+                fr.fr_adarms_gate_res_fp8(x[l], gate[n], res[n], res[n + 1],
+                                          sc[n], sh[n], EPS, q8[n], fr.Q_STATIC,
+                                          56.0, None, T, H, fr.F16, stream=stream)
+                fr.fr_qkv_normrope_kvwrite(qkv[l], None, None, EPS, pos, 1e4,
+                                           fr.ROPE_HALF, q_out[l], kc[l], vc[l],
+                                           table, 1, d["page_size"], 1, None, T,
+                                           d["Hq"], d["Hkv"], d["D"], fr.F16,
+                                           stream=stream)
+                n += 1
+
+    run()
+    stream.synchronize()
+    # eager launches (host-bound reference)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / 3
+
+    graph = HipGraph(stream, run)
+    nodes = graph.kernel_node_count()
+    for _ in range(5):
+        graph.launch()
+    stream.synchronize()
+    times = []
+    for _ in range(replays):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.launch()
+        b.record(stream)
+        stream.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    t = np.array(times)
+    return {
+        "kernel_nodes": nodes,
+        "replay_us_p10": round(float(np.percentile(t, 10)), 1),
+        "replay_us_p50": round(float(np.percentile(t, 50)), 1),
+        "replay_us_p90": round(float(np.percentile(t, 90)), 1),
+        "us_per_op_p50": round(float(np.percentile(t, 50)) / nodes, 3),
+        "eager_us_per_op": round(eager_us / nodes, 3),
+    }
+
+
+def run_small(torch, fr, workloads, dev, stream):
+    """Standalone (outside any graph) hipEvent medians at 10 tokens."""
+    out = {}
+    ri = workloads.resid_rmsnorm_inputs(10, 1024, workloads.F16, 101)
+    x, r, w = dev(ri["x"]), dev(ri["residual"]), dev(ri["weight"])
+    ro = torch.empty_like(x)
+    q = torch.empty((10, 1024), dtype=torch.uint8, device="cuda")
+
+    def a():
+        fr.fr_resid_rmsnorm_fp8(x, r, ro, w, fr.W_NONE, EPS, q, fr.Q_STATIC,
+                                56.0, None, 10, 1024, fr.F16, stream=stream)
+
+    gi = workloads.gated_act_inputs(10, 6144, workloads.BF16, 104)
+    gu = dev(gi["gate_up"])
+    gq = torch.empty((10, 6144), dtype=torch.uint8, device="cuda")
+    gs = torch.empty((10, 48), dtype=torch.float32, device="cuda")
+
+    def c():
+        fr.fr_gated_act_fp8(gu, fr.ACT_SWIGLU, gq, gs, 10, 6144, fr.BF16,
+                            stream=stream)
+
+    for name, f in (("resid_rmsnorm_fp8_T10_H1024", a), ("gated_act_fp8_T10_I6144", c)):
+        for _ in range(5):
+            f()
+        ts = []
+        for _ in range(50):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            f()
+            e1.record(stream)
+            stream.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        out[name + "_us_p50"] = round(float(np.median(ts)), 2)
+    return out
+
+
+def cpu_baseline(budget_s):
+    """The oracle (plain C, double precision, one thread) on a row sample of
+    the same four ops, sized to about `budget_s` seconds; reported in the
+    same unit (algorithmic GB/s)."""
+    import oracle
+    import workloads
+    nb = op_bytes()
+    # rows per op in the sample, and the fraction of the 8192-token op they are
+    rows = {"resid_rmsnorm_fp8": 64, "adarms_gate_res_fp8": 256,
+            "qkv_normrope_kvwrite": 32, "gated_act_fp8": 16}
+    ri = workloads.resid_rmsnorm_inputs(rows["resid_rmsnorm_fp8"], 4096,
+                                        workloads.BF16, 105, outliers=True)
+    ai = workloads.adarms_inputs(rows["adarms_gate_res_fp8"], 1024, workloads.F16, 102)
+    qi = workloads.qkv_inputs(rows["qkv_normrope_kvwrite"], 32, 8, 128,
+                              workloads.BF16, 103, page_size=16, num_pages=512)
+    gi = workloads.gated_act_inputs(rows["gated_act_fp8"], 12288, workloads.BF16,
+                                    105, outliers=True)
+    oracle.lib()
+
+    def one_pass():
+        oracle.resid_rmsnorm_fp8(ri["x"], ri["residual"], ri["weight"],
+                                 oracle.W_MUL, EPS, oracle.Q_TOKEN, 0.0, oracle.BF16)
+        oracle.adarms_gate_res_fp8(ai["x"], ai["gate"], ai["residual"],
+                                   ai["ada_scale"], ai["ada_shift"], EPS,
+                                   oracle.Q_STATIC, 56.0, oracle.F16)
+        oracle.qkv_normrope_kvwrite(qi["qkv"], qi["q_norm_w"], qi["k_norm_w"], EPS,
+                                    qi["positions"], 1e6, oracle.ROPE_HALF,
+                                    qi["k_cache"], qi["v_cache"], qi["page_table"],
+                                    16, 32, 8, 128, oracle.BF16)
+        oracle.gated_act_fp8(gi["gate_up"], oracle.ACT_SWIGLU, oracle.BF16)
+
+    sample_bytes = sum(nb[k] * rows[k] / T_BIG for k in rows)
+    t0 = time.perf_counter()
+    one_pass()
+    t1 = time.perf_counter()
+    passes = max(1, int(budget_s / max(t1 - t0, 1e-3)) - 1)
+    for _ in range(passes):
+        one_pass()
+    t2 = time.perf_counter()
+    secs = (t2 - t0) / (passes + 1)
+    return {
+        "value": round(sample_bytes / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{passes + 1} passes over the four ops on row subsets of the "
+                  f"8192-token step ({rows}); {secs * 1e3:.1f} ms per pass",
+        "seconds": round(t2 - t0, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * fr.h -- C ABI of the fused, memory-bound layer-boundary kernels for
+ * small-batch transformer inference on MI355X (gfx950).
+ *
+ * Library: memory_bound_amd/libfrhip.so (HIP, gfx950 only).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees, copies or synchronises; it keeps no state.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *  - Arguments are validated on the host before any HIP call.  On error the
+ *    call returns a nonzero fr_status and launches nothing.
+ *  - On success each call enqueues exactly ONE kernel on `stream`, so it
+ *    captures into a hipGraph as one node.  T == 0 returns FR_OK and
+ *    launches nothing.
+ *  - A launch failure is returned as FR_ERR_LAUNCH (no synchronisation, so
+ *    faults inside the kernel surface at the caller's next sync).
+ *  - Tensors are contiguous and row-major; every pointer must be 16-byte
+ *    aligned (4-byte for the int32 arrays).
+ *  - 16-bit tensors are float16 or bfloat16 bit patterns (`dtype`); FP8
+ *    outputs are OCP E4M3 ("e4m3fn") codes: 1 sign, 4 exponent bits (bias
+ *    7), 3 mantissa bits, subnormals, largest finite value 448 (0x7E/0xFE),
+ *    no infinities.  A torch float8_e4m3fn tensor viewed as uint8 matches.
+ *    Values are clamped to +-448 before rounding (saturating), rounding is
+ *    to nearest, ties to even.
+ *  - Arithmetic is fp32 (the RMSNorm sum of squares is accumulated in
+ *    fp64).  A value that an op stores and also consumes (the new residual)
+ *    is consumed in its stored, rounded form; every other intermediate stays
+ *    in fp32 until its single store.
+ *  - Results are deterministic: no atomics in value paths; repeated calls
+ *    on the same inputs give bit-identical outputs.
+ *
+ * The operations are defined on these web pages (cited by title/section):
+ *   [FR]   "FlashRT cross-layer fusion" article: section 二 (per-layer
+ *          fused-kernel table; 2.1 naming "_fp8", "_noweight"; 2.2 QKV
+ *          post-processing), section 三 (gate/residual/AdaRMSNorm/FP8 kernel;
+ *          (1+weight) pre-fold), section 六 ("_merged", "_static").
+ *   [SM89] "sm89 prefill FFN megakernel" issue: Phase 2 (gated activation +
+ *          per-token block-128 FP8 with no intermediate bf16 rounding) and
+ *          the correctness notes (every scale row must be written).
+ *   [FP]   "Falcon-Perception inference engine" article: third technique
+ *          (gated activation read from interleaved [g0,u0,g1,u1,...]) and
+ *          the paged KV cache behind its CUDA-graph decode.
+ */
+#ifndef FR_H
+#define FR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FR_ABI_VERSION 1
+
+typedef enum {
+    FR_OK = 0,
+    FR_ERR_NULL = 1,         /* a required pointer is NULL */
+    FR_ERR_SHAPE = 2,        /* negative/zero/non-multiple size */
+    FR_ERR_DTYPE = 3,        /* dtype not FR_F16 / FR_BF16 */
+    FR_ERR_ALIGN = 4,        /* pointer not 16-byte (int32 arrays: 4-byte) aligned */
+    FR_ERR_MODE = 5,         /* unknown enum value, or bad scalar (eps, scale, theta) */
+    FR_ERR_UNSUPPORTED = 6,  /* width above what one kernel row handles */
+    FR_ERR_LAUNCH = 7        /* the HIP launch returned an error */
+} fr_status;
+
+typedef enum { FR_F16 = 0, FR_BF16 = 1 } fr_dtype;
+
+/* RMSNorm weight: none ("_noweight": weight pre-folded into the next GEMM,
+ * [FR 2.1, 三]), y*w, or y*(1+w). */
+typedef enum { FR_W_NONE = 0, FR_W_MUL = 1, FR_W_ONE_PLUS = 2 } fr_wmode;
+
+/* FP8 quantisation: static multiplier ("_static", [FR 六]) or per-token
+ * dynamic dequant scale. */
+typedef enum { FR_Q_STATIC = 0, FR_Q_TOKEN = 1 } fr_qmode;
+
+/* Gate activation: SiLU (SwiGLU), GELU tanh approximation (GeGLU), ReLU^2. */
+typedef enum { FR_ACT_SWIGLU = 0, FR_ACT_GEGLU_TANH = 1, FR_ACT_SQRELU = 2 } fr_act;
+
+/* RoPE pairing: element i with i+D/2 ("rotate_half", [FR 2.2]), or
+ * element 2i with 2i+1. */
+typedef enum { FR_ROPE_HALF = 0, FR_ROPE_INTERLEAVED = 1 } fr_rope;
+
+/*
+ * (a) Residual add + RMSNorm + FP8 quantisation  [FR 二 table step 1, 2.1]
+ *
+ *   residual_out[t,j] = round_dtype(x[t,j] + residual[t,j])
+ *   rstd_t  = 1 / sqrt(mean_j(residual_out[t,j]^2) + eps)
+ *   y[t,j]  = residual_out[t,j] * rstd_t * W_j,  W_j = 1 | w_j | 1 + w_j
+ *   FR_Q_STATIC: out_fp8[t,j] = E4M3(y[t,j] * static_scale)
+ *   FR_Q_TOKEN:  out_scales[t] = max(max_j |y[t,j]|, 1e-10) / 448 (fp32),
+ *                out_fp8[t,j] = E4M3(y[t,j] / out_scales[t])
+ *
+ *   x, residual, residual_out: [T,H] dtype.  residual_out may alias
+ *     residual (in place); no other overlap is allowed.
+ *   weight: [H] dtype; ignored (may be NULL) for FR_W_NONE.
+ *   out_fp8: [T,H] uint8.  out_scales: [T] fp32 dequant scales, required
+ *     for FR_Q_TOKEN, ignored for FR_Q_STATIC.
+ *   static_scale: the quantisation MULTIPLIER (e.g. 448/8 = 56); the
+ *     matching dequant scale is 1/static_scale.  Must be finite and > 0.
+ *   eps >= 0 and finite.  H % 16 == 0, 16 <= H <= 32768.
+ */
+int fr_resid_rmsnorm_fp8(const void* x, const void* residual, void* residual_out,
+                         const void* weight, int wmode, float eps,
+                         uint8_t* out_fp8, int qmode, float static_scale,
+                         float* out_scales, int64_t T, int64_t H, int dtype,
+                         void* stream);
+
+/*
+ * (a') Gate multiply + residual + adaptive RMSNorm + FP8  [FR 三]
+ *
+ *   residual_out[t,j] = round_dtype(residual[t,j] + gate[t,j] * x[t,j]),
+ *     the exact value rounded once
+ *   y[t,j] = residual_out[t,j] * rstd_t * (1 + ada_scale[t,j]) + ada_shift[t,j]
+ *   quantised as in (a).
+ *
+ *   x, gate, residual, residual_out, ada_scale, ada_shift: [T,H] dtype
+ *   (one modulation vector per token).  residual_out may alias residual.
+ *   Other arguments as in (a).
+ */
+int fr_adarms_gate_res_fp8(const void* x, const void* gate, const void* residual,
+                           void* residual_out, const void* ada_scale,
+                           const void* ada_shift, float eps, uint8_t* out_fp8,
+                           int qmode, float static_scale, float* out_scales,
+                           int64_t T, int64_t H, int dtype, void* stream);
+
+/*
+ * (b) Packed-QKV split + per-head Q/K RMSNorm + RoPE + paged KV write
+ *     [FR 二 table step 3, 2.2; FP paged cache]
+ *
+ *   qkv row t = [Q heads: Hq*D | K heads: Hkv*D | V heads: Hkv*D], each head
+ *     D-contiguous.
+ *   For a Q or K head v (D values): if its norm weight is non-NULL,
+ *     v = v * rstd(v) * w with rstd over the D values and one weight [D]
+ *     shared by all heads; then RoPE at p = positions[t]: pair i
+ *     (0 <= i < D/2) turns by p * rope_theta^(-2i/D); then one rounding.
+ *   q_out[t,h,:] = Q head h;   k_cache[slot,g,:] = K head g;
+ *   v_cache[slot,g,:] = V head g copied bit for bit (V is never normed or
+ *   rotated).
+ *   slot = page_table[p / page_size] * page_size + p % page_size.
+ *   If p < 0, p / page_size >= page_table_len, or the page id is outside
+ *   [0, num_pages), the token's K/V writes are skipped and, when err_flag
+ *   is non-NULL, bit 0 of *err_flag is set (atomic OR); q_out is still
+ *   written.  Cache slots no token maps to are never touched.  Two tokens
+ *   of one call that map to the same slot leave one of the two writes
+ *   (which one is unspecified).
+ *
+ *   qkv: [T,(Hq+2Hkv)*D] dtype.  q_norm_w, k_norm_w: [D] dtype or NULL.
+ *   positions: [T] int32 (device).  page_table: [page_table_len] int32.
+ *   q_out: [T,Hq,D].  k_cache, v_cache: [num_pages, page_size, Hkv, D].
+ *   positions and page_table are read on the device, so a captured graph
+ *   can be replayed with new positions.
+ *   D % 16 == 0, 16 <= D <= 256; Hq, Hkv >= 1; rope_theta > 1 and finite.
+ */
+int fr_qkv_normrope_kvwrite(const void* qkv, const void* q_norm_w,
+                            const void* k_norm_w, float eps,
+                            const int32_t* positions, float rope_theta,
+                            int rope_style, void* q_out, void* k_cache,
+                            void* v_cache, const int32_t* page_table,
+                            int32_t page_table_len, int32_t page_size,
+                            int32_t num_pages, int32_t* err_flag, int64_t T,
+                            int32_t Hq, int32_t Hkv, int32_t D, int dtype,
+                            void* stream);
+
+/*
+ * (c) Gated activation on interleaved gate/up + per-token block-128 FP8
+ *     [SM89 Phase 2; FP third technique; FR 二 table steps 8-10]
+ *
+ *   gate_up row t = [g0, u0, g1, u1, ...] (2I values).
+ *   h[t,j] = act(g_j) * u_j in fp32, not rounded in between;
+ *     SiLU(g) = g / (1 + e^-g); GELU_tanh(g) = 0.5 g (1 + tanh(sqrt(2/pi)
+ *     (g + 0.044715 g^3))); ReLU^2(g) = max(g, 0)^2.
+ *   For each block b of 128 consecutive outputs of a row:
+ *     out_scales[t,b] = max(max |h|, 1e-10) / 448 (fp32 dequant scale),
+ *     out_fp8[t,j] = E4M3(h[t,j] / out_scales[t,b]).
+ *   Every scale entry is written.
+ *
+ *   gate_up: [T,2I] dtype.  out_fp8: [T,I] uint8.  out_scales: [T, I/128]
+ *   fp32, row-major.  I % 128 == 0, I >= 128.
+ */
+int fr_gated_act_fp8(const void* gate_up, int act, uint8_t* out_fp8,
+                     float* out_scales, int64_t T, int64_t I, int dtype,
+                     void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fr_status_string(int status);
+
+/* FR_ABI_VERSION of the built library. */
+int fr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FR_H */

@@ -1,0 +1,127 @@
+// fr_act.hip -- gated activation on interleaved gate/up + per-token block-128
+// FP8 quantisation (op c), one kernel.
+//
+// Definitions: "sm89 prefill FFN megakernel" issue, Phase 2 (silu(g)*u with
+// per-token block-128 FP8 output, no intermediate bf16 rounding) and its
+// correctness notes (every scale entry must be written); "Falcon-Perception
+// inference engine" article, third technique (the gate kernel reads
+// interleaved [g0, u0, g1, u1, ...] in one pass); "FlashRT cross-layer
+// fusion" article, section 二 table steps 8-10 (GELU * up + FP8 fused).
+//
+// Mapping: each 32-bit word of a bf16/fp16 row holds one (g, u) pair, so one
+// 16-byte chunk yields 4 outputs.  A block of 128 outputs is 32 chunks: the
+// lower or upper 32 lanes of one 128-bit wave load.  A wave walks U
+// consecutive block pairs of one row (U loads in flight per lane, each load
+// instruction a contiguous 1 KB span).  The block maximum is a DPP row
+// reduction followed by one permlane16 swap; the scale division uses an fma
+// correction so the fp32 scale is the correctly rounded amax / 448.
+#include "fr_device.h"
+#include "fr_launch.h"
+
+namespace fr {
+
+enum { ACT_SWIGLU = 0, ACT_GEGLU_TANH = 1, ACT_SQRELU = 2 };
+
+constexpr int kActU = 4;   // block pairs per wave
+
+template <int ACT>
+__device__ __forceinline__ float gate_act(float g) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    if constexpr (ACT == ACT_SWIGLU) {
+        // g * sigmoid(g) = g / (1 + 2^(-g log2 e))
+        const float e = __builtin_amdgcn_exp2f(-g * kLog2e);
+        return g * __builtin_amdgcn_rcpf(1.0f + e);
+    } else if constexpr (ACT == ACT_GEGLU_TANH) {
+        // 0.5 g (1 + tanh z) = g * sigmoid(2z), z = sqrt(2/pi)(g + 0.044715 g^3);
+        // the sigmoid form has no cancellation for negative z.
+        constexpr float c1 = 2.0f * 0.7978845608028654f * kLog2e;
+        constexpr float c3 = 2.0f * 0.7978845608028654f * 0.044715f * kLog2e;
+        const float g2 = g * g;
+        const float arg = g * fmaf(c3, g2, c1);            // 2z log2 e
+        const float e = __builtin_amdgcn_exp2f(-arg);
+        return g * __builtin_amdgcn_rcpf(1.0f + e);
+    } else {
+        const float r = fmaxf(g, 0.0f);
+        return r * r;
+    }
+}
+
+template <int DT, int ACT>
+__global__ __launch_bounds__(256) void k_act(ActArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wid >= a.waves) return;                          // whole wave exits
+    const int64_t t = wid / a.wpr;
+    const int wc = (int)(wid - t * a.wpr);
+    const int half = lane >> 5;
+    const int cb = lane & 31;                            // chunk within block
+
+    const char* row = (const char*)a.gu + t * (int64_t)a.I * 4;
+    uint8_t* orow = a.out + t * (int64_t)a.I;
+    float* srow = a.scales + t * (int64_t)a.nb;
+
+    u32x4 in[kActU];
+    bool ok[kActU];
+#pragma unroll
+    for (int k = 0; k < kActU; ++k) {
+        const int b = (wc * kActU + k) * 2 + half;
+        ok[k] = b < a.nb;
+        in[k] = (u32x4){0, 0, 0, 0};
+        if (ok[k]) in[k] = ld128(row + (int64_t)b * 512 + cb * 16);
+    }
+
+    constexpr float kInv448 = 1.0f / 448.0f;
+#pragma unroll
+    for (int k = 0; k < kActU; ++k) {
+        float h[4];
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float g = lo16<DT>(in[k][e]);
+            const float u = hi16<DT>(in[k][e]);
+            h[e] = gate_act<ACT>(g) * u;
+            m = fmaxf(m, fabsf(h[e]));
+        }
+        // Block maximum over 32 lanes (all 64 lanes take part).
+        m = group_reduce<16>(m, OpMax());
+        m = rows_pair(m, OpMax());
+        const float amax = fmaxf(m, 1e-10f);
+        // s = amax / 448 correctly rounded: q0 = amax * (1/448), then one fma
+        // correction with the exact remainder amax - q0 * 448.
+        const float q0 = amax * kInv448;
+        const float s = fmaf(fmaf(-q0, 448.0f, amax), kInv448, q0);
+        const float inv = __builtin_amdgcn_rcpf(s);
+        const int b = (wc * kActU + k) * 2 + half;
+        if (ok[k]) {
+            const u32 q = pack_e4m3x4(h[0] * inv, h[1] * inv, h[2] * inv, h[3] * inv);
+            *reinterpret_cast<u32*>(orow + (int64_t)b * 128 + cb * 4) = q;
+            if (cb == 0) srow[b] = s;
+        }
+    }
+}
+
+template <int DT>
+static hipError_t launch_act_dt(const ActArgs& a, int act, hipStream_t s) {
+    const void* fn;
+    switch (act) {
+    case ACT_SWIGLU: fn = (const void*)k_act<DT, ACT_SWIGLU>; break;
+    case ACT_GEGLU_TANH: fn = (const void*)k_act<DT, ACT_GEGLU_TANH>; break;
+    default: fn = (const void*)k_act<DT, ACT_SQRELU>; break;
+    }
+    ActArgs copy = a;
+    void* args[] = {&copy};
+    const unsigned blocks = (unsigned)((a.waves + 3) / 4);
+    return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, s);
+}
+
+hipError_t launch_act(const ActArgs& in, int dtype, int act, hipStream_t s) {
+    ActArgs a = in;
+    a.nb = a.I / 128;
+    const int per_wave = 2 * kActU;                      // blocks per wave
+    a.wpr = (a.nb + per_wave - 1) / per_wave;
+    a.waves = a.T * a.wpr;
+    return dtype == DT_BF16 ? launch_act_dt<DT_BF16>(a, act, s)
+                            : launch_act_dt<DT_F16>(a, act, s);
+}
+
+}  // namespace fr

@@ -1,0 +1,197 @@
+// fr_device.h -- gfx950 device helpers shared by the fused kernels:
+// 16-bit storage conversions, saturating OCP E4M3 packing, and wave64
+// cross-lane reductions built from DPP row operations and the gfx950
+// permlane swaps (no LDS traffic inside a wavefront).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fr {
+
+typedef uint32_t u32;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+// ---------------------------------------------------------------------------
+// 16-bit storage types, two values per 32-bit word (element 2k in the low
+// half, 2k+1 in the high half).
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float lo16(u32 w) {
+    if constexpr (DT == DT_BF16)
+        return __uint_as_float(w << 16);
+    else
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+
+template <int DT>
+__device__ __forceinline__ float hi16(u32 w) {
+    if constexpr (DT == DT_BF16)
+        return __uint_as_float(w & 0xffff0000u);
+    else
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Round two fp32 values to the storage type (nearest, ties to even) and pack.
+template <int DT>
+__device__ __forceinline__ u32 pack16(float a, float b) {
+    if constexpr (DT == DT_BF16) {
+        bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
+        return __builtin_bit_cast(u32, v);
+    } else {
+        f16x2 v = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(u32, v);
+    }
+}
+
+// r + p rounded to fp32 with round-to-odd: the exact error of the fp32 sum
+// (TwoSum) decides whether an even result is moved one ulp towards the exact
+// value.  Rounding this value once more to a format with at most 22 bits of
+// precision (fp16, bf16) gives the correctly rounded exact sum, because fp32
+// keeps at least two extra bits.
+__device__ __forceinline__ float add_round_odd(float r, float p) {
+    const float s = r + p;
+    const float bb = s - r;
+    const float e = (r - (s - bb)) + (p - bb);
+    u32 sb = __float_as_uint(s);
+    if (e != 0.0f && (sb & 1u) == 0u)
+        sb = ((e > 0.0f) == (s > 0.0f)) ? sb + 1u : sb - 1u;
+    return __uint_as_float(sb);
+}
+
+// ---------------------------------------------------------------------------
+// OCP E4M3 ("fn") packing.  v_cvt_pk_fp8_f32 rounds to nearest-even with
+// subnormals but turns magnitudes above 464 into NaN, so values are clamped
+// to +-448 first (med3), which makes the conversion saturating.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sat448(float v) {
+    return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+}
+
+__device__ __forceinline__ u32 pack_e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+    return (u32)w;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions.  DPP row operations combine lanes inside a 16-lane
+// row: quad_perm [1,0,3,2] (pairs), quad_perm [2,3,0,1] (quads),
+// row_half_mirror (8 lanes), row_mirror (16 lanes).  After the first k steps
+// every lane holds the result over its aligned group of 2^k lanes.  The
+// gfx950 permlane16/32 swaps then combine rows.  Every lane ends with the
+// same value, and the combination order is fixed (deterministic).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    u32x2 w = __builtin_bit_cast(u32x2, v);
+    w.x = (u32)__builtin_amdgcn_update_dpp(0, (int)w.x, CTRL, 0xF, 0xF, true);
+    w.y = (u32)__builtin_amdgcn_update_dpp(0, (int)w.y, CTRL, 0xF, 0xF, true);
+    return __builtin_bit_cast(double, w);
+}
+
+enum { DPP_PAIR = 0xB1, DPP_QUAD = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140 };
+
+struct OpSum {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+    __device__ __forceinline__ double operator()(double a, double b) const { return a + b; }
+};
+struct OpMax {
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// Reduce over aligned groups of G lanes (G = 1, 2, 4, 8 or 16).
+template <int G, class Op>
+__device__ __forceinline__ float group_reduce(float v, Op op) {
+    if constexpr (G >= 2) v = op(v, dpp_f<DPP_PAIR>(v));
+    if constexpr (G >= 4) v = op(v, dpp_f<DPP_QUAD>(v));
+    if constexpr (G >= 8) v = op(v, dpp_f<DPP_HALF_MIRROR>(v));
+    if constexpr (G >= 16) v = op(v, dpp_f<DPP_MIRROR>(v));
+    return v;
+}
+
+// Combine 16-lane rows pairwise (rows 0+1, rows 2+3).
+template <class Op>
+__device__ __forceinline__ float rows_pair(float v, Op op) {
+    u32 u = __builtin_bit_cast(u32, v);
+    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return op(__builtin_bit_cast(float, (u32)p[0]), __builtin_bit_cast(float, (u32)p[1]));
+}
+
+// Combine the two 32-lane halves.
+template <class Op>
+__device__ __forceinline__ float halves(float v, Op op) {
+    u32 u = __builtin_bit_cast(u32, v);
+    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return op(__builtin_bit_cast(float, (u32)p[0]), __builtin_bit_cast(float, (u32)p[1]));
+}
+
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+    v = group_reduce<16>(v, op);
+    v = rows_pair(v, op);
+    return halves(v, op);
+}
+
+__device__ __forceinline__ double swap16_sum(double v) {
+    u32x2 w = __builtin_bit_cast(u32x2, v);
+    auto px = __builtin_amdgcn_permlane16_swap(w.x, w.x, false, false);
+    auto py = __builtin_amdgcn_permlane16_swap(w.y, w.y, false, false);
+    u32x2 a = {(u32)px[0], (u32)py[0]}, b = {(u32)px[1], (u32)py[1]};
+    return __builtin_bit_cast(double, a) + __builtin_bit_cast(double, b);
+}
+
+__device__ __forceinline__ double swap32_sum(double v) {
+    u32x2 w = __builtin_bit_cast(u32x2, v);
+    auto px = __builtin_amdgcn_permlane32_swap(w.x, w.x, false, false);
+    auto py = __builtin_amdgcn_permlane32_swap(w.y, w.y, false, false);
+    u32x2 a = {(u32)px[0], (u32)py[0]}, b = {(u32)px[1], (u32)py[1]};
+    return __builtin_bit_cast(double, a) + __builtin_bit_cast(double, b);
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+    v += dpp_d<DPP_PAIR>(v);
+    v += dpp_d<DPP_QUAD>(v);
+    v += dpp_d<DPP_HALF_MIRROR>(v);
+    v += dpp_d<DPP_MIRROR>(v);
+    v = swap16_sum(v);
+    return swap32_sum(v);
+}
+
+// ---------------------------------------------------------------------------
+// Global memory access: 128-bit vector loads/stores.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld128(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 ld128_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st128(void* p, u32x4 v) {
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ void st128_stream(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st64(void* p, u32x2 v) {
+    *reinterpret_cast<u32x2*>(p) = v;
+}
+__device__ __forceinline__ void st64_stream(void* p, u32x2 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace fr

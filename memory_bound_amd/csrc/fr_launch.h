@@ -1,0 +1,69 @@
+// fr_launch.h -- host-side launch descriptors shared by the kernel files and
+// the C-ABI layer.  Each launcher enqueues exactly one kernel on `stream` via
+// hipLaunchKernel (which reports launch errors directly, without touching the
+// thread's sticky error state) and returns its hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fr {
+
+// Residual add + RMSNorm (+ optional adaptive modulation) + FP8.
+struct NormArgs {
+    const void* x;          // [T,H]
+    const void* gate;       // [T,H]   (adaptive variant only)
+    const void* res;        // [T,H]
+    void* res_out;          // [T,H]
+    const void* w;          // [H]     (plain variant, FR_W_MUL / FR_W_ONE_PLUS)
+    const void* ada_scale;  // [T,H]   (adaptive variant only)
+    const void* ada_shift;  // [T,H]   (adaptive variant only)
+    uint8_t* out;           // [T,H]
+    float* scales;          // [T]     (FR_Q_TOKEN)
+    int64_t T;
+    int H;
+    int nw;                 // wavefronts per row (block = 64*nw threads)
+    int wmode;
+    int qmode;
+    float eps;
+    float static_scale;
+};
+
+// Packed QKV split + per-head norm + RoPE + paged KV write.
+struct QkvArgs {
+    const void* qkv;
+    const void* qw;
+    const void* kw;
+    const int32_t* pos;
+    const int32_t* table;
+    void* q_out;
+    void* kc;
+    void* vc;
+    int32_t* err;
+    int64_t T;
+    int64_t tasks;          // T * groups
+    int Hq, Hkv, D;
+    int groups;             // head groups (one wavefront each) per token
+    int table_len, page_size, num_pages;
+    int style;
+    float eps;
+    float theta;
+};
+
+// Gated activation on interleaved gate/up + block-128 FP8.
+struct ActArgs {
+    const void* gu;         // [T,2I]
+    uint8_t* out;           // [T,I]
+    float* scales;          // [T,I/128]
+    int64_t T;
+    int64_t waves;          // T * wpr
+    int I;
+    int nb;                 // I / 128
+    int wpr;                // wavefronts per row
+};
+
+hipError_t launch_norm(const NormArgs& a, int dtype, bool adaptive, hipStream_t s);
+hipError_t launch_qkv(const QkvArgs& a, int dtype, hipStream_t s);
+hipError_t launch_act(const ActArgs& a, int dtype, int act, hipStream_t s);
+
+}  // namespace fr

@@ -1,0 +1,163 @@
+"""The C-ABI library loads, exports every entry point that include/fr.h
+declares, and rejects bad arguments on the host before any HIP call (CPU
+only: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import memory_bound_amd as fr
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "fr.h")
+
+# fake, 16-byte aligned, never dereferenced device addresses
+A, B, C, D_, E, F, G = (0x10000 * (i + 1) for i in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_ops_and_helpers():
+    names = declared_functions()
+    assert names == sorted([
+        "fr_resid_rmsnorm_fp8", "fr_adarms_gate_res_fp8",
+        "fr_qkv_normrope_kvwrite", "fr_gated_act_fp8", "fr_status_string",
+        "fr_abi_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", fr.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\S+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(fr.lib, name)
+    # nothing else with the public prefix leaks out
+    assert {n for n in exported if n.startswith("fr_")} == set(declared_functions())
+
+
+def test_abi_version_and_status_strings():
+    assert fr.abi_version() == 1
+    for s in range(8):
+        assert fr.status_string(s).startswith("FR_")
+    assert fr.status_string(99) == "unknown fr_status"
+
+
+def rms(**kw):
+    args = dict(x=A, residual=B, residual_out=C, weight=D_, wmode=fr.W_NONE,
+                eps=1e-6, out_fp8=E, qmode=fr.Q_STATIC, static_scale=56.0,
+                out_scales=F, T=10, H=1024, dtype=fr.F16)
+    args.update(kw)
+    L = fr.lib
+    return L.fr_resid_rmsnorm_fp8(*(fr._ptr(args[k]) if k in (
+        "x", "residual", "residual_out", "weight", "out_fp8", "out_scales")
+        else args[k] for k in ("x", "residual", "residual_out", "weight",
+                               "wmode", "eps", "out_fp8", "qmode",
+                               "static_scale", "out_scales", "T", "H",
+                               "dtype")), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), fr.FR_ERR_NULL),
+    (dict(out_fp8=None), fr.FR_ERR_NULL),
+    (dict(wmode=fr.W_MUL, weight=None), fr.FR_ERR_NULL),
+    (dict(qmode=fr.Q_TOKEN, out_scales=None), fr.FR_ERR_NULL),
+    (dict(x=A + 8), fr.FR_ERR_ALIGN),
+    (dict(out_fp8=E + 4), fr.FR_ERR_ALIGN),
+    (dict(H=1000), fr.FR_ERR_SHAPE),
+    (dict(H=0), fr.FR_ERR_SHAPE),
+    (dict(T=-1), fr.FR_ERR_SHAPE),
+    (dict(H=32768 + 16), fr.FR_ERR_UNSUPPORTED),
+    (dict(dtype=2), fr.FR_ERR_DTYPE),
+    (dict(wmode=3), fr.FR_ERR_MODE),
+    (dict(qmode=2), fr.FR_ERR_MODE),
+    (dict(eps=-1.0), fr.FR_ERR_MODE),
+    (dict(eps=float("nan")), fr.FR_ERR_MODE),
+    (dict(static_scale=0.0), fr.FR_ERR_MODE),
+    (dict(static_scale=float("inf")), fr.FR_ERR_MODE),
+    (dict(T=0), fr.FR_OK),
+])
+def test_resid_rmsnorm_validation(kw, status):
+    assert rms(**kw) == status
+
+
+def test_adarms_validation():
+    L = fr.lib
+    ok = [A, B, C, D_, E, F, 1e-6, G, fr.Q_STATIC, 56.0, None, 10, 1024,
+          fr.F16, None]
+    assert L.fr_adarms_gate_res_fp8(*ok[:11], 0, *ok[12:]) == fr.FR_OK
+    bad = list(ok)
+    bad[1] = None
+    assert L.fr_adarms_gate_res_fp8(*bad) == fr.FR_ERR_NULL
+    bad = list(ok)
+    bad[4] = E + 2
+    assert L.fr_adarms_gate_res_fp8(*bad) == fr.FR_ERR_ALIGN
+    bad = list(ok)
+    bad[8] = fr.Q_TOKEN
+    assert L.fr_adarms_gate_res_fp8(*bad) == fr.FR_ERR_NULL
+    bad = list(ok)
+    bad[12] = 24
+    assert L.fr_adarms_gate_res_fp8(*bad) == fr.FR_ERR_SHAPE
+
+
+def qkv(**kw):
+    args = dict(qkv=A, q_norm_w=None, k_norm_w=None, eps=1e-6, positions=B,
+                rope_theta=1e4, rope_style=fr.ROPE_HALF, q_out=C, k_cache=D_,
+                v_cache=E, page_table=F, page_table_len=1, page_size=1024,
+                num_pages=1, err_flag=None, T=10, Hq=8, Hkv=1, D=256,
+                dtype=fr.F16)
+    args.update(kw)
+    order = ["qkv", "q_norm_w", "k_norm_w", "eps", "positions", "rope_theta",
+             "rope_style", "q_out", "k_cache", "v_cache", "page_table",
+             "page_table_len", "page_size", "num_pages", "err_flag", "T", "Hq",
+             "Hkv", "D", "dtype"]
+    return fr.lib.fr_qkv_normrope_kvwrite(*[args[k] for k in order], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkv=None), fr.FR_ERR_NULL),
+    (dict(positions=None), fr.FR_ERR_NULL),
+    (dict(page_table=None), fr.FR_ERR_NULL),
+    (dict(D=100), fr.FR_ERR_SHAPE),
+    (dict(D=512), fr.FR_ERR_UNSUPPORTED),
+    (dict(Hkv=0), fr.FR_ERR_SHAPE),
+    (dict(page_size=0), fr.FR_ERR_SHAPE),
+    (dict(page_table_len=0), fr.FR_ERR_SHAPE),
+    (dict(num_pages=0), fr.FR_ERR_SHAPE),
+    (dict(rope_style=2), fr.FR_ERR_MODE),
+    (dict(rope_theta=1.0), fr.FR_ERR_MODE),
+    (dict(rope_theta=float("nan")), fr.FR_ERR_MODE),
+    (dict(q_norm_w=G + 8), fr.FR_ERR_ALIGN),
+    (dict(positions=B + 2), fr.FR_ERR_ALIGN),
+    (dict(err_flag=G + 1), fr.FR_ERR_ALIGN),
+    (dict(dtype=-1), fr.FR_ERR_DTYPE),
+    (dict(T=0), fr.FR_OK),
+])
+def test_qkv_validation(kw, status):
+    assert qkv(**kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 0, B, C, 10, 6144, fr.BF16), fr.FR_ERR_NULL),
+    ((A, 0, B, None, 10, 6144, fr.BF16), fr.FR_ERR_NULL),
+    ((A, 3, B, C, 10, 6144, fr.BF16), fr.FR_ERR_MODE),
+    ((A, 0, B, C, 10, 6100, fr.BF16), fr.FR_ERR_SHAPE),
+    ((A, 0, B, C, -2, 6144, fr.BF16), fr.FR_ERR_SHAPE),
+    ((A, 0, B + 4, C, 10, 6144, fr.BF16), fr.FR_ERR_ALIGN),
+    ((A, 0, B, C, 10, 6144, 5), fr.FR_ERR_DTYPE),
+    ((A, 0, B, C, 0, 6144, fr.BF16), fr.FR_OK),
+])
+def test_gated_act_validation(args, status):
+    assert fr.lib.fr_gated_act_fp8(*args, None) == status
+
+
+def test_binding_raises_on_bad_arguments():
+    with pytest.raises(fr.FrError) as e:
+        fr.fr_gated_act_fp8(A, 0, B, C, 10, 100, fr.BF16, stream=0)
+    assert e.value.status == fr.FR_ERR_SHAPE

@@ -1,0 +1,125 @@
+"""The decoder-step chain under a HIP graph: 10 flow steps x 18 layers x
+(gate + residual + AdaRMSNorm + FP8, then QKV split + RoPE + KV write) at 10
+tokens, captured once and replayed, against the oracle running the same 360
+calls in the same order."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import announce, check16, check_exact, check_fp8, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+F16 = 0
+EPS = 1e-6
+THETA = 1e4
+
+
+def oracle_chain(ci):
+    d = ci["dims"]
+    L, S, T, H = d["layers"], d["steps"], d["T"], d["H"]
+    Hq, Hkv, D, P = d["Hq"], d["Hkv"], d["D"], d["page_size"]
+    res = np.empty((L * S + 1, T, H), np.uint16)
+    res[0] = ci["r0"]
+    q8 = np.empty((L * S, T, H), np.uint8)
+    q_out = np.empty((L, T, Hq, D), np.uint16)
+    kc, vc = ci["k_cache"].copy(), ci["v_cache"].copy()
+    n = 0
+    for s in range(S):
+        for l in range(L):
+            res[n + 1], q8[n], _ = oracle.adarms_gate_res_fp8(
+                ci["x"][l], ci["gate"][n], res[n], ci["ada_scale"][n],
+                ci["ada_shift"][n], EPS, oracle.Q_STATIC, 56.0, F16)
+            q_out[l], err = oracle.qkv_normrope_kvwrite(
+                ci["qkv"][l], None, None, EPS, ci["positions"], THETA,
+                oracle.ROPE_HALF, kc[l], vc[l], ci["page_table"], P, Hq, Hkv,
+                D, F16)
+            assert err == 0
+            n += 1
+    return res, q8, q_out, kc, vc
+
+
+class DeviceChain:
+    def __init__(self, fr, ci, stream):
+        self.fr, self.ci, self.stream = fr, ci, stream
+        d = ci["dims"]
+        self.d = d
+        L, S, T, H = d["layers"], d["steps"], d["T"], d["H"]
+        self.x = to_dev(ci["x"])
+        self.qkv = to_dev(ci["qkv"])
+        self.gate = to_dev(ci["gate"])
+        self.sc = to_dev(ci["ada_scale"])
+        self.sh = to_dev(ci["ada_shift"])
+        self.res = torch.empty((L * S + 1, T, H), dtype=torch.int16, device="cuda")
+        self.res[0] = to_dev(ci["r0"])
+        self.q8 = torch.empty((L * S, T, H), dtype=torch.uint8, device="cuda")
+        self.q_out = torch.empty((L, T, d["Hq"], d["D"]), dtype=torch.int16,
+                                 device="cuda")
+        self.kc = to_dev(ci["k_cache"])
+        self.vc = to_dev(ci["v_cache"])
+        self.pos = to_dev(ci["positions"])
+        self.table = to_dev(ci["page_table"])
+
+    def poison(self):
+        self.res[1:].fill_(0x7E01)
+        self.q8.fill_(0x7F)
+        self.q_out.fill_(0x7E01)
+
+    def run(self):
+        fr, d, s = self.fr, self.d, self.stream
+        L, S, T, H = d["layers"], d["steps"], d["T"], d["H"]
+        n = 0
+        for _ in range(S):
+            for l in range(L):
+                fr.fr_adarms_gate_res_fp8(
+                    self.x[l], self.gate[n], self.res[n], self.res[n + 1],
+                    self.sc[n], self.sh[n], EPS, self.q8[n], fr.Q_STATIC, 56.0,
+                    None, T, H, fr.F16, stream=s)
+                fr.fr_qkv_normrope_kvwrite(
+                    self.qkv[l], None, None, EPS, self.pos, THETA, fr.ROPE_HALF,
+                    self.q_out[l], self.kc[l], self.vc[l], self.table, 1,
+                    d["page_size"], 1, None, T, d["Hq"], d["Hkv"], d["D"],
+                    fr.F16, stream=s)
+                n += 1
+
+    def host(self):
+        return (to_host(self.res, np.uint16), to_host(self.q8, np.uint8),
+                to_host(self.q_out, np.uint16), to_host(self.kc, np.uint16),
+                to_host(self.vc, np.uint16))
+
+
+def compare(got, want):
+    res_g, q8_g, q_g, kc_g, vc_g = got
+    res_o, q8_o, q_o, kc_o, vc_o = want
+    check_exact(res_g, res_o, "residual chain")
+    check_fp8(q8_g, q8_o, "fp8 outputs")
+    check16(q_g, q_o, F16, "q_out")
+    written = kc_o != workloads.SENTINEL
+    check_exact(kc_g[~written], kc_o[~written], "k_cache untouched")
+    check16(kc_g[written], kc_o[written], F16, "k_cache")
+    check_exact(vc_g, vc_o, "v_cache")
+
+
+def test_decode_chain_eager_and_graph():
+    import memory_bound_amd as fr
+    from memory_bound_amd.hipgraph import HipGraph
+    announce("decode chain: 18 layers x 10 steps, eager then hipGraph")
+    ci = workloads.chain_inputs()
+    want = oracle_chain(ci)
+    stream = torch.cuda.Stream()
+    chain = DeviceChain(fr, ci, stream)
+    chain.poison()
+    chain.run()                                  # eager (also loads kernels)
+    stream.synchronize()
+    compare(chain.host(), want)
+
+    graph = HipGraph(stream, chain.run)
+    assert graph.kernel_node_count() == 360
+    for _ in range(3):
+        chain.poison()                           # eager work between replays
+        torch.cuda.synchronize()
+        graph.launch()
+        stream.synchronize()
+        compare(chain.host(), want)
