@@ -1,0 +1,134 @@
+"""Summarise rocprofv3 output of the benchmark into profiles/.
+
+Kernel durations (per-kernel launch count, average, median, min):
+    rocprofv3 --kernel-trace --stats -d <dir> -o bench -- python3 bench.py --steps 10 --no-cpu-baseline
+    python3 bench_profile.py trace <dir>/bench_results.db
+
+HBM byte counters of the 8192-token ops:
+    rocprofv3 --pmc FETCH_SIZE -d <dir_f> -o fetch -- python3 bench.py --pmc-pass
+    rocprofv3 --pmc WRITE_SIZE -d <dir_w> -o write -- python3 bench.py --pmc-pass
+    python3 bench_profile.py pmc <dir_f>/fetch_results.db <dir_w>/write_results.db
+
+The --pmc-pass run first copies 1 GiB device-to-device three times (the HIP
+runtime's copyBuffer kernel, known traffic: 1 GiB read + 1 GiB written).
+Each counter is scaled by known bytes / counted bytes of that copy, then
+reported per launch for every fused-op kernel next to its algorithmic bytes.
+Writes profiles/hbm_traffic_T8192.txt and, for the dominant kernel,
+profiles/gated_act_fp8_T8192_I12288_pmc.json (with the hash of the kernel
+source it was taken on; bench.py uses the traffic only while it matches).
+"""
+import collections
+import hashlib
+import json
+import os
+import sqlite3
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GIB = 1 << 30
+
+KERNELS = {  # kernel name prefix -> (op, algorithmic read bytes, write bytes)
+    "void fr::k_norm<1, 2, 1, true>": ("resid_rmsnorm_fp8 T=8192 H=4096 bf16 MUL TOKEN",
+                                        8192 * 4096 * 4 + 4096 * 2, 8192 * 4096 * 3 + 8192 * 4),
+    "void fr::k_norm<0, 2, 3, true>": ("adarms_gate_res_fp8 T=8192 H=1024 f16 STATIC",
+                                        8192 * 1024 * 10, 8192 * 1024 * 3),
+    "void fr::k_qkv<1, 8, true>": ("qkv_normrope_kvwrite T=8192 32/8x128 bf16",
+                                    8192 * 48 * 128 * 2 + 8192 * 4 + 512 * 4 + 512,
+                                    8192 * 48 * 128 * 2),
+    "void fr::k_act<1, 0>": ("gated_act_fp8 T=8192 I=12288 bf16 SwiGLU",
+                              8192 * 24576 * 2, 8192 * 12288 + 8192 * 96 * 4),
+}
+
+
+def per_kernel(db):
+    c = sqlite3.connect(db)
+    vals = collections.defaultdict(list)
+    for name, val, grid in c.execute(
+            "select kernel_name, value, grid_size from counters_collection order by dispatch_id"):
+        vals[(name, grid)].append(val * 1024.0)          # KiB -> bytes
+    return vals
+
+
+def trace(db, out_name="kernel_trace_bench_T8192_and_T10_chain.txt"):
+    c = sqlite3.connect(db)
+    groups = collections.defaultdict(list)
+    for name, dur, grid, wg in c.execute(
+            "select name, duration, grid_x, workgroup_x from kernels"):
+        groups[(name, grid, wg)].append(dur / 1000.0)
+    lines = [
+        "Kernel durations from rocprofv3 --kernel-trace (MI355X, gfx950), microseconds",
+        "commands:",
+        "  rocprofv3 --kernel-trace --stats -d gpurun_out/prof -o bench -- python3 -u bench.py --steps 10 --no-cpu-baseline --chain-replays 5",
+        "  python3 bench_profile.py trace gpurun_out/prof/bench_results.db",
+        "grid = work-items; the 8192-token ops are the large grids, the 10-token",
+        "chain ops (2 x 180 per graph replay) the small ones.",
+        "",
+        f"{'calls':>6s} {'avg':>10s} {'median':>10s} {'min':>10s} {'grid':>9s} {'wg':>5s}  kernel",
+    ]
+    for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        d = sorted(d)
+        lines.append(f"{len(d):6d} {sum(d) / len(d):10.3f} {d[len(d) // 2]:10.3f} "
+                     f"{d[0]:10.3f} {grid:9d} {wg:5d}  {name[:90]}")
+    with open(os.path.join(HERE, "profiles", out_name), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def pmc(fetch_db, write_db):
+    f, w = per_kernel(fetch_db), per_kernel(write_db)
+    # the three 1 GiB copies: copyBuffer launches with the largest grid
+    cal = [k for k in f if k[0].startswith("__amd_rocclr_copyBuffer")]
+    big = max(cal, key=lambda k: k[1])
+    f_scale = GIB / (sum(f[big]) / len(f[big]))
+    w_scale = GIB / (sum(w[big]) / len(w[big]))
+    lines = [
+        "HBM traffic per launch, rocprofv3 PMC counters (MI355X, gfx950)",
+        "commands:",
+        "  rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch -- python3 -u bench.py --pmc-pass",
+        "  rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write -- python3 -u bench.py --pmc-pass",
+        "  python3 bench_profile.py pmc gpurun_out/pmc_fetch/fetch_results.db gpurun_out/pmc_write/write_results.db",
+        f"calibration: 1 GiB device copy ({big[0]}, grid {big[1]}):",
+        f"  FETCH_SIZE counted {sum(f[big]) / len(f[big]) / 1e6:.2f} MB -> scale {f_scale:.4f}",
+        f"  WRITE_SIZE counted {sum(w[big]) / len(w[big]) / 1e6:.2f} MB -> scale {w_scale:.4f}",
+        "",
+        f"{'kernel / op':58s} {'read MB':>9s} {'alg':>9s} {'write MB':>9s} {'alg':>9s} {'total/alg':>9s}",
+    ]
+    out = {}
+    for (name, grid), fv in sorted(f.items()):
+        for prefix, (op, alg_r, alg_w) in KERNELS.items():
+            if name.startswith(prefix) and (name, grid) in w:
+                rd = sum(fv) / len(fv) * f_scale
+                wr = sum(w[(name, grid)]) / len(w[(name, grid)]) * w_scale
+                ratio = (rd + wr) / (alg_r + alg_w)
+                lines.append(f"{op:58s} {rd / 1e6:9.2f} {alg_r / 1e6:9.2f} "
+                             f"{wr / 1e6:9.2f} {alg_w / 1e6:9.2f} {ratio:9.4f}")
+                out[prefix] = {"op": op, "read_bytes": rd, "write_bytes": wr,
+                               "alg_read_bytes": alg_r, "alg_write_bytes": alg_w,
+                               "launches": len(fv)}
+    os.makedirs(os.path.join(HERE, "profiles"), exist_ok=True)
+    with open(os.path.join(HERE, "profiles", "hbm_traffic_T8192.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    dom = out.get("void fr::k_act<1, 0>")
+    if dom:
+        with open(os.path.join(HERE, "memory_bound_amd", "csrc", "fr_act.hip"), "rb") as fh:
+            sha = hashlib.sha256(fh.read()).hexdigest()[:16]
+        rec = {"kernel": "fr::k_act<bf16, SwiGLU>", "workload": "T=8192 I=12288 bf16",
+               "source_sha256_16": sha,
+               "hbm_bytes_per_launch": round(dom["read_bytes"] + dom["write_bytes"]),
+               "read_bytes_per_launch": round(dom["read_bytes"]),
+               "write_bytes_per_launch": round(dom["write_bytes"]),
+               "fetch_scale": f_scale, "write_scale": w_scale}
+        with open(os.path.join(HERE, "profiles", "gated_act_fp8_T8192_I12288_pmc.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+
+
+if __name__ == "__main__":
+    os.makedirs(os.path.join(HERE, "profiles"), exist_ok=True)
+    if sys.argv[1] == "trace":
+        trace(sys.argv[2])
+    elif sys.argv[1] == "pmc":
+        pmc(sys.argv[2], sys.argv[3])
+    else:
+        sys.exit("usage: bench_profile.py trace <db> | pmc <fetch_db> <write_db>")

@@ -65,6 +65,18 @@ __device__ __forceinline__ float add_round_odd(float r, float p) {
     return __uint_as_float(sb);
 }
 
+// Round-to-odd of the exact value p + e, where p = fp32(p + e) and e is the
+// (small) remainder: if e != 0 and p's last significand bit is even, step one
+// ulp towards the exact value.  A later rounding of the result to a format
+// with at least two fewer significand bits (e4m3 has 4) is then the correct
+// rounding of p + e.
+__device__ __forceinline__ float round_odd(float p, float e) {
+    u32 b = __float_as_uint(p);
+    if (e != 0.0f && (b & 1u) == 0u)
+        b = ((__float_as_uint(e) ^ b) >> 31) ? b - 1u : b + 1u;
+    return __uint_as_float(b);
+}
+
 // ---------------------------------------------------------------------------
 // OCP E4M3 ("fn") packing.  v_cvt_pk_fp8_f32 rounds to nearest-even with
 // subnormals but turns magnitudes above 464 into NaN, so values are clamped

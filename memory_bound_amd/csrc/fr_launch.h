@@ -22,7 +22,8 @@ struct NormArgs {
     float* scales;          // [T]     (FR_Q_TOKEN)
     int64_t T;
     int H;
-    int nw;                 // wavefronts per row (block = 64*nw threads)
+    int nw;                 // wavefronts per row
+    int rpb;                // rows per workgroup (block = 64*nw*rpb threads)
     int wmode;
     int qmode;
     float eps;
@@ -41,9 +42,11 @@ struct QkvArgs {
     void* vc;
     int32_t* err;
     int64_t T;
-    int64_t tasks;          // T * groups
+    int64_t tasks;          // T * wpt wavefronts
     int Hq, Hkv, D;
-    int groups;             // head groups (one wavefront each) per token
+    int groups;             // head groups (64/LP heads each) per token
+    int gpw;                // head groups per wavefront
+    int wpt;                // wavefronts per token
     int table_len, page_size, num_pages;
     int style;
     float eps;

@@ -13,25 +13,57 @@
 // 16-byte chunks (8 values); lane l of wave w owns chunks
 // k*64*nw + w*64 + l (k < CPL), so every load and store instruction of a
 // wave touches one contiguous 1 KB span.  All input chunks are loaded before
-// any arithmetic.  The new residual is rounded to the storage type, written,
-// and kept packed in registers; its sum of squares is accumulated in fp64
-// (squares of 16-bit values are exact in fp32; the fp64 sum makes rstd
-// independent of the summation order).  The row sum is a DPP + permlane wave
-// reduction, with LDS only for the cross-wave step.  FP8 codes are packed
-// with v_cvt_pk_fp8_f32 after a +-448 clamp and written 8 bytes per chunk.
+// any arithmetic (a ragged row re-loads its last chunk instead of branching).
+// The new residual is rounded to the storage type, written, and kept packed
+// in registers; its sum of squares is accumulated in fp64 (squares of 16-bit
+// values are exact in fp32, and the fp64 sum is exact for any realistic row,
+// so rstd does not depend on the summation order).  The row sum is a DPP +
+// permlane wave reduction, with LDS only for the cross-wave step.
+//
+// FP8 decision of op (a): the code of element j is E(y_j * K) with
+// y_j = ro_j * rstd * W_j and K the static multiplier or 1/scale.  The kernel
+// forms t_j = ro_j * W_j (exact in fp32 for 16-bit operands) and the
+// per-row factor rstd * K in fp64, split into two fp32 halves; the product is
+// evaluated as a float pair and rounded to odd, so the e4m3 rounding that
+// follows is the rounding of the exact value to within ~2^-46.  Without this,
+// rows where rstd cancels against the per-token scale (no weight) put many
+// values exactly on e4m3 rounding midpoints and fp32 noise picks the side.
 #include "fr_device.h"
 #include "fr_launch.h"
 
 namespace fr {
 
-template <int DT, int CPL, bool ADA>
+enum { M_NONE = 0, M_MUL = 1, M_ONE_PLUS = 2, M_ADA = 3 };
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_in(const void* p) {
+    if constexpr (NT) return ld128_stream(p); else return ld128(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st_out(void* p, u32x4 v) {
+    if constexpr (NT) st128_stream(p, v); else st128(p, v);
+}
+template <bool NT>
+__device__ __forceinline__ void st_out(void* p, u32x2 v) {
+    if constexpr (NT) st64_stream(p, v); else st64(p, v);
+}
+
+// NT: non-temporal loads of the streamed inputs and stores of the outputs
+// (the norm weight is re-read by every row and stays cached).
+template <int DT, int CPL, int MODE, bool NT>
 __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
+    constexpr bool ADA = MODE == M_ADA;
+    constexpr bool HAS_W = MODE == M_MUL || MODE == M_ONE_PLUS;
     __shared__ double red_ss[8];
     __shared__ float red_max[8];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t t = blockIdx.x;
+    const int wave = threadIdx.x >> 6;                   // wave in the workgroup
+    const int rw = wave / a.nw;                          // row in the workgroup
+    const int ww = wave - rw * a.nw;                     // wave in the row
+    const int64_t t_row = (int64_t)blockIdx.x * a.rpb + rw;
+    const bool row_ok = t_row < a.T;
+    const int64_t t = row_ok ? t_row : a.T - 1;          // in-bounds duplicate
     const int C = a.H >> 3;
     const int stride = a.nw * 64;
     const int64_t rb = t * (int64_t)a.H * 2;   // row offset in bytes
@@ -44,26 +76,24 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     bool ok[CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
-        const int c = k * stride + wave * 64 + lane;
+        const int c = k * stride + ww * 64 + lane;
         ok[k] = c < C;
-        xv[k] = rv[k] = gv[k] = sv[k] = hv[k] = wv[k] = (u32x4){0, 0, 0, 0};
-        if (ok[k]) {
-            xv[k] = ld128(xr + c * 16);
-            rv[k] = ld128(rr + c * 16);
-            if constexpr (ADA) {
-                gv[k] = ld128((const char*)a.gate + rb + c * 16);
-                sv[k] = ld128((const char*)a.ada_scale + rb + c * 16);
-                hv[k] = ld128((const char*)a.ada_shift + rb + c * 16);
-            } else {
-                if (a.wmode != 0) wv[k] = ld128((const char*)a.w + c * 16);
-            }
+        const int cl = ok[k] ? c : C - 1;            // in-bounds duplicate
+        xv[k] = ld_in<NT>(xr + cl * 16);
+        rv[k] = ld_in<NT>(rr + cl * 16);
+        if constexpr (ADA) {
+            gv[k] = ld_in<NT>((const char*)a.gate + rb + cl * 16);
+            sv[k] = ld_in<NT>((const char*)a.ada_scale + rb + cl * 16);
+            hv[k] = ld_in<NT>((const char*)a.ada_shift + rb + cl * 16);
         }
+        if constexpr (HAS_W) wv[k] = ld128((const char*)a.w + cl * 16);
     }
 
     // Pass 1: new residual, rounded once; sum of squares of the stored value.
     double ss0 = 0.0, ss1 = 0.0;
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
+        double c0 = 0.0, c1 = 0.0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float h0, h1;
@@ -77,122 +107,193 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
                 h0 = lo16<DT>(xv[k][e]) + lo16<DT>(rv[k][e]);
                 h1 = hi16<DT>(xv[k][e]) + hi16<DT>(rv[k][e]);
             }
-            const u32 b = ok[k] ? pack16<DT>(h0, h1) : 0u;
+            const u32 b = pack16<DT>(h0, h1);
             rv[k][e] = b;
             const double r0 = (double)lo16<DT>(b), r1 = (double)hi16<DT>(b);
-            ss0 = fma(r0, r0, ss0);
-            ss1 = fma(r1, r1, ss1);
+            c0 = fma(r0, r0, c0);
+            c1 = fma(r1, r1, c1);
         }
-        if (ok[k]) st128(ror + (k * stride + wave * 64 + lane) * 16, rv[k]);
+        if (ok[k]) {                                 // skip duplicated chunks
+            ss0 += c0;
+            ss1 += c1;
+            if (row_ok) st_out<NT>(ror + (k * stride + ww * 64 + lane) * 16, rv[k]);
+        }
     }
 
     double ss = wave_sum_d(ss0 + ss1);
     if (a.nw > 1) {
         if (lane == 0) red_ss[wave] = ss;
         __syncthreads();
-        ss = red_ss[0];
-        for (int w = 1; w < a.nw; ++w) ss += red_ss[w];
+        ss = red_ss[rw * a.nw];
+        for (int w = 1; w < a.nw; ++w) ss += red_ss[rw * a.nw + w];
     }
-    const float rstd = (float)(1.0 / sqrt(ss / (double)a.H + (double)a.eps));
-
-    // Pass 2: normalised (and modulated) values.
-    float y[CPL][8];
-    float amax = 0.0f;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float n0 = lo16<DT>(rv[k][e]) * rstd;
-            const float n1 = hi16<DT>(rv[k][e]) * rstd;
-            float y0, y1;
-            if constexpr (ADA) {
-                y0 = fmaf(n0, 1.0f + lo16<DT>(sv[k][e]), lo16<DT>(hv[k][e]));
-                y1 = fmaf(n1, 1.0f + hi16<DT>(sv[k][e]), hi16<DT>(hv[k][e]));
-            } else {
-                y0 = n0;
-                y1 = n1;
-                if (a.wmode == 1) {
-                    y0 *= lo16<DT>(wv[k][e]);
-                    y1 *= hi16<DT>(wv[k][e]);
-                } else if (a.wmode == 2) {
-                    y0 *= 1.0f + lo16<DT>(wv[k][e]);
-                    y1 *= 1.0f + hi16<DT>(wv[k][e]);
-                }
-            }
-            y[k][2 * e] = y0;
-            y[k][2 * e + 1] = y1;
-            amax = fmaxf(amax, fmaxf(fabsf(y0), fabsf(y1)));
-        }
-    }
-
-    float mult = a.static_scale;
-    if (a.qmode == 1) {
-        amax = wave_reduce(amax, OpMax());
-        if (a.nw > 1) {
-            if (lane == 0) red_max[wave] = amax;
-            __syncthreads();
-            amax = red_max[0];
-            for (int w = 1; w < a.nw; ++w) amax = fmaxf(amax, red_max[w]);
-        }
-        const float s = fmaxf(amax, 1e-10f) / 448.0f;   // IEEE division
-        mult = 1.0f / s;
-        if (wave == 0 && lane == 0) a.scales[t] = s;
-    }
-
+    const double rstd_d = 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
     uint8_t* orow = a.out + t * (int64_t)a.H;
+
+    if constexpr (ADA) {
+        // Pass 2 (adaptive): y = n * (1 + scale) + shift in fp32.
+        const float rstd = (float)rstd_d;
+        float y[CPL][8];
+        float amax = 0.0f;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-        if (!ok[k]) continue;
-        u32x2 q;
-        q.x = pack_e4m3x4(y[k][0] * mult, y[k][1] * mult, y[k][2] * mult, y[k][3] * mult);
-        q.y = pack_e4m3x4(y[k][4] * mult, y[k][5] * mult, y[k][6] * mult, y[k][7] * mult);
-        st64(orow + (k * stride + wave * 64 + lane) * 8, q);
+        for (int k = 0; k < CPL; ++k) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float n0 = lo16<DT>(rv[k][e]) * rstd;
+                const float n1 = hi16<DT>(rv[k][e]) * rstd;
+                const float y0 = fmaf(n0, 1.0f + lo16<DT>(sv[k][e]), lo16<DT>(hv[k][e]));
+                const float y1 = fmaf(n1, 1.0f + hi16<DT>(sv[k][e]), hi16<DT>(hv[k][e]));
+                y[k][2 * e] = y0;
+                y[k][2 * e + 1] = y1;
+                if (ok[k]) amax = fmaxf(amax, fmaxf(fabsf(y0), fabsf(y1)));
+            }
+        }
+        float mult = a.static_scale;
+        if (a.qmode == 1) {
+            amax = wave_reduce(amax, OpMax());
+            if (a.nw > 1) {
+                if (lane == 0) red_max[wave] = amax;
+                __syncthreads();
+                amax = red_max[rw * a.nw];
+                for (int w = 1; w < a.nw; ++w) amax = fmaxf(amax, red_max[rw * a.nw + w]);
+            }
+            const float s = (float)((double)fmaxf(amax, 1e-10f) / 448.0);
+            mult = 1.0f / s;
+            if (row_ok && ww == 0 && lane == 0) a.scales[t] = s;
+        }
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            if (!ok[k] || !row_ok) continue;
+            u32x2 q;
+            q.x = pack_e4m3x4(y[k][0] * mult, y[k][1] * mult, y[k][2] * mult, y[k][3] * mult);
+            q.y = pack_e4m3x4(y[k][4] * mult, y[k][5] * mult, y[k][6] * mult, y[k][7] * mult);
+            st_out<NT>(orow + (k * stride + ww * 64 + lane) * 8, q);
+        }
+    } else {
+        // Pass 2 (plain): t = ro * W (float pair for the (1+w) case).
+        float th[CPL][8], tl[CPL][8];
+        float tmax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const u32 rw = rv[k][e >> 1];
+                const float ro = (e & 1) ? hi16<DT>(rw) : lo16<DT>(rw);
+                float hi = ro, lo = 0.0f;
+                if constexpr (MODE == M_MUL) {
+                    const u32 ww = wv[k][e >> 1];
+                    hi = ro * ((e & 1) ? hi16<DT>(ww) : lo16<DT>(ww));     // exact
+                } else if constexpr (MODE == M_ONE_PLUS) {
+                    const u32 ww = wv[k][e >> 1];
+                    const float c = 1.0f + ((e & 1) ? hi16<DT>(ww) : lo16<DT>(ww));
+                    hi = ro * c;
+                    lo = fmaf(ro, c, -hi);                                  // exact remainder
+                }
+                th[k][e] = hi;
+                tl[k][e] = lo;
+                if (ok[k]) tmax = fmaxf(tmax, fabsf(hi));
+            }
+        }
+        double K = rstd_d * (double)a.static_scale;
+        if (a.qmode == 1) {
+            tmax = wave_reduce(tmax, OpMax());
+            if (a.nw > 1) {
+                if (lane == 0) red_max[wave] = tmax;
+                __syncthreads();
+                tmax = red_max[rw * a.nw];
+                for (int w = 1; w < a.nw; ++w) tmax = fmaxf(tmax, red_max[rw * a.nw + w]);
+            }
+            const double amax = fmax((double)tmax * rstd_d, (double)1e-10f);
+            const float s = (float)(amax / 448.0);
+            K = rstd_d / (double)s;
+            if (row_ok && ww == 0 && lane == 0) a.scales[t] = s;
+        }
+        const float Kh = (float)K;
+        const float Kl = (float)(K - (double)Kh);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            if (!ok[k] || !row_ok) continue;
+            float q[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = th[k][e] * Kh;
+                float r = fmaf(th[k][e], Kh, -p);
+                r = fmaf(th[k][e], Kl, r);
+                if constexpr (MODE == M_ONE_PLUS) r = fmaf(tl[k][e], Kh, r);
+                q[e] = round_odd(p, r);
+            }
+            u32x2 o;
+            o.x = pack_e4m3x4(q[0], q[1], q[2], q[3]);
+            o.y = pack_e4m3x4(q[4], q[5], q[6], q[7]);
+            st_out<NT>(orow + (k * stride + ww * 64 + lane) * 8, o);
+        }
     }
 }
 
-template <int DT, bool ADA>
-static hipError_t launch_norm_dt(const NormArgs& a, int cpl, hipStream_t s) {
+template <int DT, int MODE, bool NT>
+static hipError_t launch_norm_mode(const NormArgs& a, int cpl, hipStream_t s) {
     const void* fn;
     switch (cpl) {
-    case 1: fn = (const void*)k_norm<DT, 1, ADA>; break;
-    case 2: fn = (const void*)k_norm<DT, 2, ADA>; break;
-    case 4: fn = (const void*)k_norm<DT, 4, ADA>; break;
-    default: fn = (const void*)k_norm<DT, 8, ADA>; break;
+    case 1: fn = (const void*)k_norm<DT, 1, MODE, NT>; break;
+    case 2: fn = (const void*)k_norm<DT, 2, MODE, NT>; break;
+    case 4: fn = (const void*)k_norm<DT, 4, MODE, NT>; break;
+    default: fn = (const void*)k_norm<DT, 8, MODE, NT>; break;
     }
     NormArgs copy = a;
     void* args[] = {&copy};
-    return hipLaunchKernel(fn, dim3((unsigned)a.T), dim3(64 * a.nw), args, 0, s);
+    const unsigned blocks = (unsigned)((a.T + a.rpb - 1) / a.rpb);
+    return hipLaunchKernel(fn, dim3(blocks), dim3(64 * a.nw * a.rpb), args, 0, s);
 }
 
-// Chunks per lane and wavefronts per row.  Large batches (bandwidth regime)
-// use few wavefronts per row with many chunks per lane, which keeps the whole
-// row's loads in flight per wave without any LDS step; small batches
-// (latency regime) spread each row over more wavefronts so that each lane has
-// at most two chunks of serial work.
-static void pick_norm_shape(int64_t T, int H, bool adaptive, int* cpl, int* nw) {
+template <int DT, bool NT>
+static hipError_t launch_norm_dt(const NormArgs& a, int mode, int cpl, hipStream_t s) {
+    switch (mode) {
+    case M_NONE: return launch_norm_mode<DT, M_NONE, NT>(a, cpl, s);
+    case M_MUL: return launch_norm_mode<DT, M_MUL, NT>(a, cpl, s);
+    case M_ONE_PLUS: return launch_norm_mode<DT, M_ONE_PLUS, NT>(a, cpl, s);
+    default: return launch_norm_mode<DT, M_ADA, NT>(a, cpl, s);
+    }
+}
+
+struct NormShape {
+    int cpl, nw, rpb;
+    bool nt;
+};
+
+// Launch shape: at most two 16-byte chunks per lane, so a row spreads over
+// up to 8 wavefronts (more chunks per lane only for rows wider than 8192
+// values), and in the bandwidth regime (T >= 2048) two single-wave rows per
+// workgroup and non-temporal streaming.  Measured on MI355X at T = 8192:
+// H = 4096 bf16 runs at ~75% of 8 TB/s with 4 waves x 2 chunks per row
+// (one wave x 8 chunks: 65%; without non-temporal access: 50%); H = 1024
+// fp16 adaptive at ~77% with 2 rows per workgroup.  Small batches keep the
+// outputs cacheable for the next op.
+static NormShape pick_norm_shape(int64_t T, int H, bool adaptive) {
+    (void)adaptive;
     const int C = H / 8;
-    int target = T >= 2048 ? (adaptive ? 4 : 8) : 2;
+    const bool big = T >= 2048;
     int c = 1;
-    while (c < target && c * 64 < C) c *= 2;
+    while (c < 2 && c * 64 < C) c *= 2;
     int w = (C + 64 * c - 1) / (64 * c);
     while (w > 8) {
         c *= 2;
         w = (C + 64 * c - 1) / (64 * c);
     }
-    *cpl = c;
-    *nw = w;
+    const int rpb = (big && w == 1) ? 2 : 1;
+    return {c, w, rpb, big};
 }
 
 hipError_t launch_norm(const NormArgs& in, int dtype, bool adaptive, hipStream_t s) {
     NormArgs a = in;
-    int cpl, nw;
-    pick_norm_shape(a.T, a.H, adaptive, &cpl, &nw);
-    a.nw = nw;
+    const NormShape sh = pick_norm_shape(a.T, a.H, adaptive);
+    a.nw = sh.nw;
+    a.rpb = sh.rpb;
+    const int mode = adaptive ? M_ADA : a.wmode;
     if (dtype == DT_BF16)
-        return adaptive ? launch_norm_dt<DT_BF16, true>(a, cpl, s)
-                        : launch_norm_dt<DT_BF16, false>(a, cpl, s);
-    return adaptive ? launch_norm_dt<DT_F16, true>(a, cpl, s)
-                    : launch_norm_dt<DT_F16, false>(a, cpl, s);
+        return sh.nt ? launch_norm_dt<DT_BF16, true>(a, mode, sh.cpl, s)
+                     : launch_norm_dt<DT_BF16, false>(a, mode, sh.cpl, s);
+    return sh.nt ? launch_norm_dt<DT_F16, true>(a, mode, sh.cpl, s)
+                 : launch_norm_dt<DT_F16, false>(a, mode, sh.cpl, s);
 }
 
 }  // namespace fr

@@ -7,19 +7,25 @@
 // in one lane so no cross-lane shuffle is needed) and the "Falcon-Perception
 // inference engine" article (paged KV cache written by the decode step).
 //
-// Mapping: a wave64 handles one token and a group of 64/LP heads; LP lanes
-// (a power of two >= D/16) serve one head.  Lane j of a head holds the
+// Mapping: a wave64 handles one token and `gpw` groups of 64/LP heads; LP
+// lanes (a power of two >= D/16) serve one head.  Lane j of a head holds the
 // 16-byte chunk j of the first half of the head and chunk j of the second
 // half, so each rotate-half pair (i, i+D/2) -- and each interleaved pair
-// (2i, 2i+1) -- sits in one lane's registers.  The per-head sum of squares is
-// a DPP reduction over the LP lanes.  Rotation angles are formed in fp64
-// (pos * theta^(-2i/D), reduced modulo pi/2 by a two-constant Cody-Waite
-// step with fma) and their sine/cosine come from Taylor polynomials on
-// [-pi/4, pi/4], so the angle stays exact to ~1e-16 for any int32 position.
+// (2i, 2i+1) -- sits in one lane's registers.  Each group's loads are issued
+// while the previous group is processed.  The per-head sum of squares is a DPP reduction over the LP
+// lanes.  The D/2 rotation angles of the token are shared by every head: the
+// wave computes each of them once (one or two per lane) into a per-wave LDS
+// table, then every lane reads the cos/sin of its own pairs.  Angles are
+// formed in fp64 (pos * theta^(-2i/D), reduced modulo pi/2 by a
+// two-constant Cody-Waite step with fma) and sine/cosine come from Taylor
+// polynomials on [-pi/4, pi/4], so the angle stays exact to ~1e-16 for any
+// int32 position.
 #include "fr_device.h"
 #include "fr_launch.h"
 
 namespace fr {
+
+constexpr int kQkvMaxGroups = 8;   // head groups one wave may take
 
 // sin and cos of x (radians).  k = nearest integer to x/(pi/2), r = x - k*pi/2
 // with pi/2 split into a head (the double nearest pi/2) and its tail; fma
@@ -57,23 +63,26 @@ __device__ __forceinline__ void sincos_pos(double x, float* s_out, float* c_out)
     *c_out = (float)c;
 }
 
-template <int DT, int LP>
+// NT: non-temporal loads of the packed rows and stores of Q, K and V (used
+// in the bandwidth regime, where nothing is re-read soon).
+template <int DT, int LP, bool NT>
 __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
+    __shared__ float tab[4][2][128];                     // per-wave cos / sin
+
     const int lane = threadIdx.x & 63;
-    const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (task >= a.tasks) return;                        // whole wave exits
-    const int64_t t = task / a.groups;
-    const int hg = (int)(task - t * a.groups);
+    const int wv = threadIdx.x >> 6;
+    const int64_t task = (int64_t)blockIdx.x * 4 + wv;
+    if (task >= a.tasks) return;                         // whole wave exits
+    const int64_t t = task / a.wpt;                      // token
+    const int g0 = (int)(task - t * a.wpt) * a.gpw;      // first head group
+    const int ng = min(a.gpw, a.groups - g0);            // groups of this wave
 
     constexpr int HPW = 64 / LP;
     const int NH = a.Hq + 2 * a.Hkv;
     const int D = a.D;
-    const int L = D >> 4;                               // lanes with data per head
-    const int head = hg * HPW + lane / LP;
+    const int L = D >> 4;                                // lanes with data per head
     const int j = lane & (LP - 1);
-    const bool active = (j < L) && (head < NH);
-    const bool is_q = head < a.Hq;
-    const bool is_v = head >= a.Hq + a.Hkv;
+    const int hl = lane / LP;                            // head within a group
 
     // Token metadata (uniform across the wave).
     const int pos = a.pos[t];
@@ -86,131 +95,167 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
                 slot = (int64_t)page * a.page_size + pos % a.page_size;
         }
     }
-    if (slot < 0 && hg == 0 && lane == 0 && a.err != nullptr)
+    if (slot < 0 && g0 == 0 && lane == 0 && a.err != nullptr)
         __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    const int64_t row_bytes = (int64_t)NH * D * 2;
-    const char* src = (const char*)a.qkv + t * row_bytes + (int64_t)head * D * 2;
+    // Head group g of this wave: its chunks are loaded one group ahead of
+    // the group being processed.
+    const char* rowp = (const char*)a.qkv + t * (int64_t)NH * D * 2;
     const int off0 = j * 16;                 // bytes of chunk j, first half
     const int off1 = D + j * 16;             // bytes of chunk j, second half
-
-    u32x4 c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0}, w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
-    const void* nwp = is_q ? a.qw : a.kw;
-    const bool has_norm = !is_v && nwp != nullptr;
-    if (active) {
-        c0 = ld128(src + off0);
-        c1 = ld128(src + off1);
-        if (has_norm) {
-            w0 = ld128((const char*)nwp + off0);
-            w1 = ld128((const char*)nwp + off1);
+    auto load_group = [&](int g, u32x4& x0, u32x4& x1) {
+        x0 = x1 = (u32x4){0, 0, 0, 0};
+        const int head = (g0 + g) * HPW + hl;
+        if (g < ng && j < L && head < NH) {
+            const char* src = rowp + (int64_t)head * D * 2;
+            x0 = NT ? ld128_stream(src + off0) : ld128(src + off0);
+            x1 = NT ? ld128_stream(src + off1) : ld128(src + off1);
         }
+    };
+    u32x4 n0, n1;
+    load_group(0, n0, n1);
+    u32x4 qw0 = {0, 0, 0, 0}, qw1 = qw0, kw0 = qw0, kw1 = qw0;
+    if (j < L) {
+        if (a.qw) { qw0 = ld128((const char*)a.qw + off0); qw1 = ld128((const char*)a.qw + off1); }
+        if (a.kw) { kw0 = ld128((const char*)a.kw + off0); kw1 = ld128((const char*)a.kw + off1); }
     }
 
-    if (is_v) {
-        if (active && slot >= 0) {
-            char* dst = (char*)a.vc + (slot * a.Hkv + (head - a.Hq - a.Hkv)) * (int64_t)D * 2;
-            st128(dst + off0, c0);
-            st128(dst + off1, c1);
+    // cos/sin table of the token: angle i = pos * theta^(-2i/D), i < D/2.
+    float* cs_tab = tab[wv][0];
+    float* sn_tab = tab[wv][1];
+    {
+        const double l2t = log2((double)a.theta);
+        for (int i = lane; i < (D >> 1); i += 64) {
+            const double f = exp2(-(double)(2 * i) / (double)D * l2t);
+            float sv, cv;
+            sincos_pos((double)pos * f, &sv, &cv);
+            cs_tab[i] = cv;
+            sn_tab[i] = sv;
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // This lane's pairs: rotate-half pair e = (8j+e, D/2+8j+e) turns by
+    // angle 8j+e; interleaved pair m of chunk 0 = (8j+2m, 8j+2m+1) by angle
+    // 4j+m, pair m of chunk 1 by angle D/4+4j+m.
+    float cs[8], sn[8];
+    if (j < L) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = a.style == 0 ? 8 * j + e
+                                       : (e < 4 ? 4 * j + e : (D >> 2) + 4 * j + (e - 4));
+            cs[e] = cs_tab[i];
+            sn[e] = sn_tab[i];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] = sn[e] = 0.0f;
     }
 
-    float v[16];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[2 * e] = lo16<DT>(c0[e]);
-        v[2 * e + 1] = hi16<DT>(c0[e]);
-        v[8 + 2 * e] = lo16<DT>(c1[e]);
-        v[8 + 2 * e + 1] = hi16<DT>(c1[e]);
-    }
+#pragma unroll 1
+    for (int g = 0; g < ng; ++g) {                       // uniform trip count
+        const u32x4 c0 = n0, c1 = n1;
+        load_group(g + 1, n0, n1);
+        const int head = (g0 + g) * HPW + hl;
+        const bool active = (j < L) && (head < NH);
+        const bool is_q = head < a.Hq;
+        const bool is_v = head >= a.Hq + a.Hkv;
 
-    // Per-head RMSNorm over D (all lanes take part in the reduction; lanes
-    // without data contribute zero).
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) ss = fmaf(v[e], v[e], ss);
-    ss = group_reduce<LP>(ss, OpSum());
-    if (has_norm) {
-        const float rstd = 1.0f / sqrtf(ss / (float)D + a.eps);
+        if (is_v) {
+            if (active && slot >= 0) {
+                char* dst = (char*)a.vc + (slot * a.Hkv + (head - a.Hq - a.Hkv)) * (int64_t)D * 2;
+                if constexpr (NT) {
+                    st128_stream(dst + off0, c0);
+                    st128_stream(dst + off1, c1);
+                } else {
+                    st128(dst + off0, c0);
+                    st128(dst + off1, c1);
+                }
+            }
+        }
+
+        float v[16];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            v[2 * e] = v[2 * e] * rstd * lo16<DT>(w0[e]);
-            v[2 * e + 1] = v[2 * e + 1] * rstd * hi16<DT>(w0[e]);
-            v[8 + 2 * e] = v[8 + 2 * e] * rstd * lo16<DT>(w1[e]);
-            v[8 + 2 * e + 1] = v[8 + 2 * e + 1] * rstd * hi16<DT>(w1[e]);
+            v[2 * e] = lo16<DT>(c0[e]);
+            v[2 * e + 1] = hi16<DT>(c0[e]);
+            v[8 + 2 * e] = lo16<DT>(c1[e]);
+            v[8 + 2 * e + 1] = hi16<DT>(c1[e]);
         }
-    }
 
-    if (!active || is_v) return;
+        // Per-head RMSNorm over D (every lane takes part in the reduction;
+        // lanes without data contribute zero).
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss = fmaf(v[e], v[e], ss);
+        ss = group_reduce<LP>(ss, OpSum());
+        const bool has_norm = !is_v && (is_q ? a.qw : a.kw) != nullptr;
+        if (has_norm) {
+            const u32x4 w0 = is_q ? qw0 : kw0, w1 = is_q ? qw1 : kw1;
+            const float rstd = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = v[2 * e] * rstd * lo16<DT>(w0[e]);
+                v[2 * e + 1] = v[2 * e + 1] * rstd * hi16<DT>(w0[e]);
+                v[8 + 2 * e] = v[8 + 2 * e] * rstd * lo16<DT>(w1[e]);
+                v[8 + 2 * e + 1] = v[8 + 2 * e + 1] * rstd * hi16<DT>(w1[e]);
+            }
+        }
+        if (!active || is_v) continue;
 
-    // RoPE.  Frequency index of each pair held by this lane:
-    //   rotate-half: pair e (e < 8) = elements (8j+e, D/2+8j+e), i = 8j+e
-    //   interleaved: pair m of chunk 0 = (8j+2m, 8j+2m+1), i = 4j+m;
-    //                pair m of chunk 1 = (D/2+8j+2m, ...),  i = D/4+4j+m.
-    const double l2t = log2((double)a.theta);
-    const double step = exp2(-2.0 / (double)D * l2t);          // theta^(-2/D)
-    const double p = (double)pos;
-    float sn[8], cs[8];
-    if (a.style == 0) {
-        double f = exp2(-(double)(2 * 8 * j) / (double)D * l2t);
+        if (a.style == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sincos_pos(p * f, &sn[e], &cs[e]);
-            f *= step;
-        }
+            for (int e = 0; e < 8; ++e) {
+                const float x0 = v[e], x1 = v[8 + e];
+                v[e] = fmaf(x0, cs[e], -x1 * sn[e]);
+                v[8 + e] = fmaf(x1, cs[e], x0 * sn[e]);
+            }
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x0 = v[e], x1 = v[8 + e];
-            v[e] = fmaf(x0, cs[e], -x1 * sn[e]);
-            v[8 + e] = fmaf(x1, cs[e], x0 * sn[e]);
+            for (int m = 0; m < 4; ++m) {
+                float x0 = v[2 * m], x1 = v[2 * m + 1];
+                v[2 * m] = fmaf(x0, cs[m], -x1 * sn[m]);
+                v[2 * m + 1] = fmaf(x1, cs[m], x0 * sn[m]);
+                x0 = v[8 + 2 * m];
+                x1 = v[8 + 2 * m + 1];
+                v[8 + 2 * m] = fmaf(x0, cs[4 + m], -x1 * sn[4 + m]);
+                v[8 + 2 * m + 1] = fmaf(x1, cs[4 + m], x0 * sn[4 + m]);
+            }
         }
-    } else {
-        double f0 = exp2(-(double)(2 * 4 * j) / (double)D * l2t);
-        double f1 = exp2(-(double)(2 * (D / 4 + 4 * j)) / (double)D * l2t);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            sincos_pos(p * f0, &sn[m], &cs[m]);
-            sincos_pos(p * f1, &sn[4 + m], &cs[4 + m]);
-            f0 *= step;
-            f1 *= step;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            float x0 = v[2 * m], x1 = v[2 * m + 1];
-            v[2 * m] = fmaf(x0, cs[m], -x1 * sn[m]);
-            v[2 * m + 1] = fmaf(x1, cs[m], x0 * sn[m]);
-            x0 = v[8 + 2 * m];
-            x1 = v[8 + 2 * m + 1];
-            v[8 + 2 * m] = fmaf(x0, cs[4 + m], -x1 * sn[4 + m]);
-            v[8 + 2 * m + 1] = fmaf(x1, cs[4 + m], x0 * sn[4 + m]);
-        }
-    }
 
-    u32x4 o0, o1;
+        u32x4 o0, o1;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        o0[e] = pack16<DT>(v[2 * e], v[2 * e + 1]);
-        o1[e] = pack16<DT>(v[8 + 2 * e], v[8 + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e) {
+            o0[e] = pack16<DT>(v[2 * e], v[2 * e + 1]);
+            o1[e] = pack16<DT>(v[8 + 2 * e], v[8 + 2 * e + 1]);
+        }
+        char* dst;
+        if (is_q) {
+            dst = (char*)a.q_out + ((t * a.Hq + head) * (int64_t)D) * 2;
+        } else {
+            if (slot < 0) continue;
+            dst = (char*)a.kc + (slot * a.Hkv + (head - a.Hq)) * (int64_t)D * 2;
+        }
+        if constexpr (NT) {
+            st128_stream(dst + off0, o0);
+            st128_stream(dst + off1, o1);
+        } else {
+            st128(dst + off0, o0);
+            st128(dst + off1, o1);
+        }
     }
-    char* dst;
-    if (is_q) {
-        dst = (char*)a.q_out + ((t * a.Hq + head) * (int64_t)D) * 2;
-    } else {
-        if (slot < 0) return;
-        dst = (char*)a.kc + (slot * a.Hkv + (head - a.Hq)) * (int64_t)D * 2;
-    }
-    st128(dst + off0, o0);
-    st128(dst + off1, o1);
 }
 
-template <int DT>
+template <int DT, bool NT>
 static hipError_t launch_qkv_dt(const QkvArgs& a, int lp, hipStream_t s) {
     const void* fn;
     switch (lp) {
-    case 1: fn = (const void*)k_qkv<DT, 1>; break;
-    case 2: fn = (const void*)k_qkv<DT, 2>; break;
-    case 4: fn = (const void*)k_qkv<DT, 4>; break;
-    case 8: fn = (const void*)k_qkv<DT, 8>; break;
-    default: fn = (const void*)k_qkv<DT, 16>; break;
+    case 1: fn = (const void*)k_qkv<DT, 1, NT>; break;
+    case 2: fn = (const void*)k_qkv<DT, 2, NT>; break;
+    case 4: fn = (const void*)k_qkv<DT, 4, NT>; break;
+    case 8: fn = (const void*)k_qkv<DT, 8, NT>; break;
+    default: fn = (const void*)k_qkv<DT, 16, NT>; break;
     }
     QkvArgs copy = a;
     void* args[] = {&copy};
@@ -218,6 +263,13 @@ static hipError_t launch_qkv_dt(const QkvArgs& a, int lp, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, s);
 }
 
+// Head groups per wave.  In the bandwidth regime (T >= 2048) a token's groups
+// are split over two waves, so each wave's angles serve several groups and
+// consecutive groups' loads overlap, with non-temporal streaming; measured
+// on MI355X at T = 8192 (32/8 heads x 128, 6 groups): 3 groups per wave
+// ~69% of 8 TB/s, 6 per wave 67%, 1 or 2 per wave 50-58%, and without
+// non-temporal access ~51%.  Small batches give each group its own wave,
+// trading repeated angle work for parallelism, and keep outputs cacheable.
 hipError_t launch_qkv(const QkvArgs& in, int dtype, hipStream_t s) {
     QkvArgs a = in;
     const int L = a.D / 16;
@@ -225,10 +277,19 @@ hipError_t launch_qkv(const QkvArgs& in, int dtype, hipStream_t s) {
     while (lp < L) lp *= 2;
     const int hpw = 64 / lp;
     const int NH = a.Hq + 2 * a.Hkv;
+    const bool big = a.T >= 2048;
     a.groups = (NH + hpw - 1) / hpw;
-    a.tasks = a.T * a.groups;
-    return dtype == DT_BF16 ? launch_qkv_dt<DT_BF16>(a, lp, s)
-                            : launch_qkv_dt<DT_F16>(a, lp, s);
+    if (big) {
+        a.gpw = (a.groups + 1) / 2;
+        if (a.gpw > kQkvMaxGroups) a.gpw = kQkvMaxGroups;
+    } else {
+        a.gpw = 1;
+    }
+    a.wpt = (a.groups + a.gpw - 1) / a.gpw;
+    a.tasks = a.T * a.wpt;
+    if (dtype == DT_BF16)
+        return big ? launch_qkv_dt<DT_BF16, true>(a, lp, s) : launch_qkv_dt<DT_BF16, false>(a, lp, s);
+    return big ? launch_qkv_dt<DT_F16, true>(a, lp, s) : launch_qkv_dt<DT_F16, false>(a, lp, s);
 }
 
 }  // namespace fr

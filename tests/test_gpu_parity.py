@@ -51,7 +51,8 @@ def test_resid_rmsnorm(fr, case):
     ro_o, q_o, sc_o = oracle.resid_rmsnorm_fp8(
         inp["x"], inp["residual"], inp["weight"], wmode, EPS, qmode, s, dt)
     check_exact(ro_g, ro_o, "residual_out")
-    check_fp8(q_g, q_o, "out_fp8")
+    ident = check_fp8(q_g, q_o, "out_fp8")
+    announce(f"  fp8 identical fraction {ident:.7f}")
     if qmode == oracle.Q_TOKEN:
         check_scales(sc_g, sc_o, "out_scales")
 
@@ -110,7 +111,8 @@ def test_adarms(fr, case):
         inp["x"], inp["gate"], inp["residual"], inp["ada_scale"],
         inp["ada_shift"], EPS, qmode, s, dt)
     check_exact(ro_g, ro_o, "residual_out")
-    check_fp8(q_g, q_o, "out_fp8")
+    ident = check_fp8(q_g, q_o, "out_fp8")
+    announce(f"  fp8 identical fraction {ident:.7f}")
     if qmode == oracle.Q_TOKEN:
         check_scales(sc_g, sc_o, "out_scales")
 
@@ -171,7 +173,8 @@ def test_qkv_normrope_kvwrite(fr, case):
         inp["qkv"], inp["q_norm_w"], inp["k_norm_w"], EPS, inp["positions"],
         theta, style, kc_o, vc_o, inp["page_table"], P, Hq, Hkv, D, dt)
     assert err_g == err_o == 0
-    check16(q_g, q_o, dt, "q_out")
+    same = check16(q_g, q_o, dt, "q_out")
+    announce(f"  q_out bit-identical fraction {same:.6f}")
     _check_cache(kc_g, kc_o, dt, "k_cache")
     check_exact(vc_g, vc_o, "v_cache")
 
@@ -236,8 +239,9 @@ def test_gated_act(fr, case):
     inp = workloads.gated_act_inputs(T, I, dt, seed, outliers=outl)
     q_g, sc_g = run_gated_act(fr, inp, act, dt)
     q_o, sc_o = oracle.gated_act_fp8(inp["gate_up"], act, dt)
-    check_fp8(q_g, q_o, "out_fp8")
-    check_scales(sc_g, sc_o, "out_scales")
+    ident = check_fp8(q_g, q_o, "out_fp8")
+    rel = check_scales(sc_g, sc_o, "out_scales")
+    announce(f"  fp8 identical fraction {ident:.7f}, scale max rel err {rel:.2e}")
 
 
 def test_gated_act_worked_block(fr):
