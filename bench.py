@@ -30,7 +30,7 @@ sys.path.insert(0, HERE)
 PEAK_HBM_GBS = 8000.0
 T_BIG = 8192
 SPIN_CYCLES = 40_000_000     # host-side head start before a timed region
-BATCH = 20
+GROUP_REPEATS = 3
 EPS = 1e-6
 
 
@@ -75,7 +75,7 @@ def load_traffic(kernel_file, per_launch_bytes_key):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--chain-replays", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -223,27 +223,36 @@ def main():
 
         # ---- timed region 2: each op K times back to back ----------------
         # (buffer rotation keeps every launch reading from HBM); the average
-        # launch duration of each op is its group's event time / K.
+        # launch duration of each op is its group's event time / K.  The
+        # region is run GROUP_REPEATS times and the median is reported
+        # (launch-to-launch variation on these GPUs is a few percent).
         per_op = {}
-        torch.cuda._sleep(SPIN_CYCLES)
-        marks = [ev() for _ in range(len(ops) + 1)]
-        marks[0].record(stream)
-        for j, (_, f) in enumerate(ops):
-            for k in range(args.steps):
-                f(k)
-            marks[j + 1].record(stream)
-        torch.cuda.synchronize()
-        for j, (name, _) in enumerate(ops):
-            us = marks[j].elapsed_time(marks[j + 1]) * 1e3 / args.steps
+        reps = {name: [] for name, _ in ops}
+        grouped = []
+        for _ in range(GROUP_REPEATS):
+            torch.cuda._sleep(SPIN_CYCLES)
+            marks = [ev() for _ in range(len(ops) + 1)]
+            marks[0].record(stream)
+            for j, (_, f) in enumerate(ops):
+                for k in range(args.steps):
+                    f(k)
+                marks[j + 1].record(stream)
+            torch.cuda.synchronize()
+            for j, (name, _) in enumerate(ops):
+                reps[name].append(marks[j].elapsed_time(marks[j + 1]) * 1e3 / args.steps)
+            grouped.append(marks[0].elapsed_time(marks[-1]) / args.steps)
+        for name, _ in ops:
+            us = float(np.median(reps[name]))
             per_op[name] = {
                 "bytes": nbytes[name],
                 "us_per_launch": round(us, 3),
+                "us_per_launch_repeats": [round(v, 2) for v in reps[name]],
                 "GBps": round(nbytes[name] / (us * 1e-6) / 1e9, 1),
                 "frac_of_peak": round(nbytes[name] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                 "buffer_sets": len({"resid_rmsnorm_fp8": A, "adarms_gate_res_fp8": Ad,
                                     "qkv_normrope_kvwrite": B, "gated_act_fp8": C}[name]),
             }
-        ms_grouped = marks[0].elapsed_time(marks[-1]) / args.steps
+        ms_grouped = float(np.median(grouped))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     dom = "gated_act_fp8"

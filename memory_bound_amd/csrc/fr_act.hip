@@ -11,17 +11,16 @@
 // Mapping: each 32-bit word of a bf16/fp16 row holds one (g, u) pair, so one
 // 16-byte chunk yields 4 outputs and a block of 128 outputs is 32 chunks:
 // the lower or upper 32 lanes of one 128-bit wave load, so every load
-// instruction of a wave reads one contiguous 1 KB span.  A wave walks
-// kActSteps consecutive block pairs of one row with every load issued before
-// any arithmetic; the input is read once and the outputs are written once,
-// so loads and stores are non-temporal.  The block maximum is a DPP row
+// instruction of a wave reads one contiguous 1 KB span.  A wave walks STEPS
+// consecutive block pairs of one row with every load issued before any
+// arithmetic; the input is read once, so its loads are non-temporal in the
+// bandwidth regime.  The block maximum is a DPP row
 // reduction plus one permlane16 swap.  The scale is the correctly rounded
 // amax / 448 (fma-corrected quotient); |h / scale| <= 448 (1 + 3 ulp) < 464,
 // so the e4m3 conversion never sees a value that would overflow and needs no
-// clamp.  (Measured on MI355X at 8192 x 12288: this layout with 4 steps, 4
-// waves per workgroup and non-temporal access runs at ~6.2 TB/s; 2 or 8
-// waves per workgroup, 8 or 16 steps, or 32-byte lane-contiguous chunks are
-// 5-15% slower.)
+// clamp.  (Measured on MI355X at 8192 x 12288: this layout with 4 waves per
+// workgroup is 5-15% faster than 2 or 8 waves per workgroup or 32-byte
+// lane-contiguous chunks.)
 #include "fr_device.h"
 #include "fr_launch.h"
 
@@ -29,7 +28,7 @@ namespace fr {
 
 enum { ACT_SWIGLU = 0, ACT_GEGLU_TANH = 1, ACT_SQRELU = 2 };
 
-constexpr int kActSteps = 4;   // block pairs per wave
+constexpr int kActSteps = 8;   // block pairs per wave (bandwidth regime)
 
 template <int ACT>
 __device__ __forceinline__ float gate_act(float g) {
@@ -53,7 +52,8 @@ __device__ __forceinline__ float gate_act(float g) {
     }
 }
 
-template <int DT, int ACT>
+// STEPS: block pairs per wave; NTL / NTS: non-temporal loads / stores.
+template <int DT, int ACT, int STEPS = kActSteps, bool NTL = true, bool NTS = true>
 __global__ __launch_bounds__(256) void k_act(ActArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -67,20 +67,20 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
     uint8_t* orow = a.out + t * (int64_t)a.I;
     float* srow = a.scales + t * (int64_t)a.nb;
 
-    u32x4 in[kActSteps];
-    int blk[kActSteps];
+    u32x4 in[STEPS];                                     // all loads first
+    int blk[STEPS];
 #pragma unroll
-    for (int k = 0; k < kActSteps; ++k) {
-        const int b = (wc * kActSteps + k) * 2 + half;
+    for (int k = 0; k < STEPS; ++k) {
+        const int b = (wc * STEPS + k) * 2 + half;
         blk[k] = b;
         const unsigned off = (unsigned)(b < a.nb ? b : a.nb - 1) * 512u + (unsigned)cb * 16u;
-        in[k] = ld128_stream(row + off);
+        in[k] = NTL ? ld128_stream(row + off) : ld128(row + off);
     }
 
     constexpr float kInv448 = 1.0f / 448.0f;
     float sc = 0.0f;                                     // lane i: scale of block i
 #pragma unroll
-    for (int k = 0; k < kActSteps; ++k) {
+    for (int k = 0; k < STEPS; ++k) {
         float h[4];
         float m = 0.0f;
 #pragma unroll
@@ -101,7 +101,8 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
         if (b < a.nb) {
             int q = __builtin_amdgcn_cvt_pk_fp8_f32(h[0] * inv, h[1] * inv, 0, false);
             q = __builtin_amdgcn_cvt_pk_fp8_f32(h[2] * inv, h[3] * inv, q, true);
-            __builtin_nontemporal_store((u32)q, (u32*)(orow + (unsigned)b * 128u + (unsigned)cb * 4u));
+            u32* dst = (u32*)(orow + (unsigned)b * 128u + (unsigned)cb * 4u);
+            if constexpr (NTS) __builtin_nontemporal_store((u32)q, dst); else *dst = (u32)q;
         }
         // gather the two block scales of this step into lanes 2k and 2k+1
         const int si = __builtin_bit_cast(int, s);
@@ -109,34 +110,44 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
         const float s_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(si, 32));
         sc = lane == 2 * k ? s_lo : (lane == 2 * k + 1 ? s_hi : sc);
     }
-    // one contiguous 32-byte store of the wave's 2 * kActSteps block scales
-    const int b0 = wc * kActSteps * 2;
-    if (lane < 2 * kActSteps && b0 + lane < a.nb)
-        __builtin_nontemporal_store(sc, srow + b0 + lane);
+    // one contiguous store of the wave's 2 * STEPS block scales
+    const int b0 = wc * STEPS * 2;
+    if (lane < 2 * STEPS && b0 + lane < a.nb) {
+        if constexpr (NTS) __builtin_nontemporal_store(sc, srow + b0 + lane); else srow[b0 + lane] = sc;
+    }
 }
 
-template <int DT>
-static hipError_t launch_act_dt(const ActArgs& a, int act, hipStream_t s) {
+template <int DT, int STEPS, bool NTL, bool NTS>
+static hipError_t launch_act_cfg(const ActArgs& in, int act, hipStream_t s) {
+    ActArgs a = in;
+    const int per_wave = 2 * STEPS;                      // blocks per wave
+    a.wpr = (a.nb + per_wave - 1) / per_wave;
+    a.waves = a.T * a.wpr;
     const void* fn;
     switch (act) {
-    case ACT_SWIGLU: fn = (const void*)k_act<DT, ACT_SWIGLU>; break;
-    case ACT_GEGLU_TANH: fn = (const void*)k_act<DT, ACT_GEGLU_TANH>; break;
-    default: fn = (const void*)k_act<DT, ACT_SQRELU>; break;
+    case ACT_SWIGLU: fn = (const void*)k_act<DT, ACT_SWIGLU, STEPS, NTL, NTS>; break;
+    case ACT_GEGLU_TANH: fn = (const void*)k_act<DT, ACT_GEGLU_TANH, STEPS, NTL, NTS>; break;
+    default: fn = (const void*)k_act<DT, ACT_SQRELU, STEPS, NTL, NTS>; break;
     }
-    ActArgs copy = a;
-    void* args[] = {&copy};
+    void* args[] = {&a};
     const unsigned blocks = (unsigned)((a.waves + 3) / 4);
     return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, s);
 }
 
+// Bandwidth regime (T >= 2048): 8 block pairs per wave, non-temporal loads,
+// cacheable stores.  Measured back to back on MI355X at 8192 x 12288 bf16
+// (~6.1 TB/s): 4 pairs with non-temporal stores ~3-6% slower, cacheable loads
+// ~15% slower.  Small batches: 2 block pairs per wave for more parallel waves,
+// everything cacheable for the next op.
 hipError_t launch_act(const ActArgs& in, int dtype, int act, hipStream_t s) {
     ActArgs a = in;
     a.nb = a.I / 128;
-    const int per_wave = 2 * kActSteps;                  // blocks per wave
-    a.wpr = (a.nb + per_wave - 1) / per_wave;
-    a.waves = a.T * a.wpr;
-    return dtype == DT_BF16 ? launch_act_dt<DT_BF16>(a, act, s)
-                            : launch_act_dt<DT_F16>(a, act, s);
+    const bool big = a.T >= 2048;
+    if (dtype == DT_BF16)
+        return big ? launch_act_cfg<DT_BF16, kActSteps, true, false>(a, act, s)
+                   : launch_act_cfg<DT_BF16, 2, false, false>(a, act, s);
+    return big ? launch_act_cfg<DT_F16, kActSteps, true, false>(a, act, s)
+               : launch_act_cfg<DT_F16, 2, false, false>(a, act, s);
 }
 
 }  // namespace fr

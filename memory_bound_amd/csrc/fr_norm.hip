@@ -48,9 +48,9 @@ __device__ __forceinline__ void st_out(void* p, u32x2 v) {
     if constexpr (NT) st64_stream(p, v); else st64(p, v);
 }
 
-// NT: non-temporal loads of the streamed inputs and stores of the outputs
-// (the norm weight is re-read by every row and stays cached).
-template <int DT, int CPL, int MODE, bool NT>
+// NTL / NTS: non-temporal loads of the streamed inputs / stores of the
+// outputs (the norm weight is re-read by every row and stays cached).
+template <int DT, int CPL, int MODE, bool NTL, bool NTS = NTL>
 __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     constexpr bool ADA = MODE == M_ADA;
     constexpr bool HAS_W = MODE == M_MUL || MODE == M_ONE_PLUS;
@@ -79,12 +79,12 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
         const int c = k * stride + ww * 64 + lane;
         ok[k] = c < C;
         const int cl = ok[k] ? c : C - 1;            // in-bounds duplicate
-        xv[k] = ld_in<NT>(xr + cl * 16);
-        rv[k] = ld_in<NT>(rr + cl * 16);
+        xv[k] = ld_in<NTL>(xr + cl * 16);
+        rv[k] = ld_in<NTL>(rr + cl * 16);
         if constexpr (ADA) {
-            gv[k] = ld_in<NT>((const char*)a.gate + rb + cl * 16);
-            sv[k] = ld_in<NT>((const char*)a.ada_scale + rb + cl * 16);
-            hv[k] = ld_in<NT>((const char*)a.ada_shift + rb + cl * 16);
+            gv[k] = ld_in<NTL>((const char*)a.gate + rb + cl * 16);
+            sv[k] = ld_in<NTL>((const char*)a.ada_scale + rb + cl * 16);
+            hv[k] = ld_in<NTL>((const char*)a.ada_shift + rb + cl * 16);
         }
         if constexpr (HAS_W) wv[k] = ld128((const char*)a.w + cl * 16);
     }
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
         if (ok[k]) {                                 // skip duplicated chunks
             ss0 += c0;
             ss1 += c1;
-            if (row_ok) st_out<NT>(ror + (k * stride + ww * 64 + lane) * 16, rv[k]);
+            if (row_ok) st_out<NTS>(ror + (k * stride + ww * 64 + lane) * 16, rv[k]);
         }
     }
 
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
             u32x2 q;
             q.x = pack_e4m3x4(y[k][0] * mult, y[k][1] * mult, y[k][2] * mult, y[k][3] * mult);
             q.y = pack_e4m3x4(y[k][4] * mult, y[k][5] * mult, y[k][6] * mult, y[k][7] * mult);
-            st_out<NT>(orow + (k * stride + ww * 64 + lane) * 8, q);
+            st_out<NTS>(orow + (k * stride + ww * 64 + lane) * 8, q);
         }
     } else {
         // Pass 2 (plain): t = ro * W (float pair for the (1+w) case).
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
             u32x2 o;
             o.x = pack_e4m3x4(q[0], q[1], q[2], q[3]);
             o.y = pack_e4m3x4(q[4], q[5], q[6], q[7]);
-            st_out<NT>(orow + (k * stride + ww * 64 + lane) * 8, o);
+            st_out<NTS>(orow + (k * stride + ww * 64 + lane) * 8, o);
         }
     }
 }

@@ -65,7 +65,7 @@ __device__ __forceinline__ void sincos_pos(double x, float* s_out, float* c_out)
 
 // NT: non-temporal loads of the packed rows and stores of Q, K and V (used
 // in the bandwidth regime, where nothing is re-read soon).
-template <int DT, int LP, bool NT>
+template <int DT, int LP, bool NT, bool NTS = NT>
 __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
     __shared__ float tab[4][2][128];                     // per-wave cos / sin
 
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         if (is_v) {
             if (active && slot >= 0) {
                 char* dst = (char*)a.vc + (slot * a.Hkv + (head - a.Hq - a.Hkv)) * (int64_t)D * 2;
-                if constexpr (NT) {
+                if constexpr (NTS) {
                     st128_stream(dst + off0, c0);
                     st128_stream(dst + off1, c1);
                 } else {
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
             if (slot < 0) continue;
             dst = (char*)a.kc + (slot * a.Hkv + (head - a.Hq)) * (int64_t)D * 2;
         }
-        if constexpr (NT) {
+        if constexpr (NTS) {
             st128_stream(dst + off0, o0);
             st128_stream(dst + off1, o1);
         } else {
