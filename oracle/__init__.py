@@ -92,6 +92,8 @@ def lib():
             _P, _P, _P, _F, _P, _F, _INT, _P, _P, _P, _P, _I32, _I32, _I32,
             _P, _I64, _I32, _I32, _I32, _INT]
         L.oracle_gated_act_fp8.argtypes = [_P, _INT, _P, _P, _I64, _I64, _INT]
+        L.oracle_gated_act_fp8_f64.argtypes = [_P, _INT, _P, _P, _I64, _I64]
+        L.oracle_gated_act_fp8_f64.restype = _INT
         for f in ("oracle_resid_rmsnorm_fp8", "oracle_adarms_gate_res_fp8",
                   "oracle_qkv_normrope_kvwrite", "oracle_gated_act_fp8"):
             getattr(L, f).restype = _INT
@@ -294,3 +296,44 @@ def gated_act_fp8(gate_up, act_kind, dtype):
                                     T, I, dtype)
     assert rc == 0
     return q, sc
+
+
+def gated_act_fp8_f64(gate_up, act_kind):
+    """Same as gated_act_fp8 on float64 gate/up values [T, 2I]."""
+    gate_up = _c(gate_up, np.float64)
+    T, I2 = gate_up.shape
+    I = I2 // 2
+    q = np.empty((T, I), dtype=np.uint8)
+    sc = np.empty((T, I // 128), dtype=np.float32)
+    rc = lib().oracle_gated_act_fp8_f64(_ptr(gate_up), act_kind, _ptr(q),
+                                        _ptr(sc), T, I)
+    assert rc == 0
+    return q, sc
+
+
+def dequant_blocks(codes, scales, rows_per_scale):
+    """e4m3 codes [R, K] times block dequant scales: scales[r // rows_per_scale,
+    k // 128] (rows_per_scale = 1 for per-token activation scales, 128 for
+    128 x 128 weight blocks).  Returns float64 [R, K]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    R, K = codes.shape
+    v = e4m3_table()[codes]
+    s = np.asarray(scales, dtype=np.float64)
+    s_full = np.repeat(np.repeat(s, rows_per_scale, axis=0)[:R], 128, axis=1)[:, :K]
+    return v * s_full
+
+
+def gemm_gated_act_fp8(a, a_scales, w, w_scales, act_kind):
+    """FP8 block-scaled GEMM fused with the gated activation and block-128
+    FP8 output [SM89 Phase 2]:
+      A [M, K] e4m3 with per-token block-128 dequant scales a_scales [M, K/128]
+      W [2I, K] e4m3, rows interleaved (gate row j at 2j, up row j at 2j+1),
+        with 128 x 128 block dequant scales w_scales [2I/128, K/128]
+      acc = dequant(A) @ dequant(W)^T in float64 (numpy matmul)
+      then act(acc[:, 2j]) * acc[:, 2j+1] and block-128 quantisation.
+    Returns (codes uint8 [M, I], scales float32 [M, I/128], acc float64)."""
+    A = dequant_blocks(a, a_scales, 1)
+    W = dequant_blocks(w, w_scales, 128)
+    acc = A @ W.T
+    q, sc = gated_act_fp8_f64(acc, act_kind)
+    return q, sc, acc

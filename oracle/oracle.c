@@ -452,24 +452,40 @@ int oracle_qkv_normrope_kvwrite(const uint16_t* qkv, const uint16_t* q_norm_w,
  *   gate_up row t = [g0, u0, g1, u1, ...] (2I values)
  *   h_j = act(g_j) * u_j, kept unrounded
  *   for each block b of 128 consecutive outputs: scale[t, b] = amax/448,
- *   code = E(h / scale). */
-int oracle_gated_act_fp8(const uint16_t* gate_up, int act, uint8_t* out_fp8,
-                         float* out_scales, int64_t T, int64_t I, int dtype)
+ *   code = E(h / scale).
+ * The _f64 form takes the gate/up values in double (the GEMM-fused op feeds
+ * it the exact product of the dequantised operands). */
+int oracle_gated_act_fp8_f64(const double* gate_up, int act, uint8_t* out_fp8,
+                             float* out_scales, int64_t T, int64_t I)
 {
     const int64_t B = 128;
     double h[128];
     for (int64_t t = 0; t < T; ++t) {
-        const uint16_t* gu = gate_up + t * 2 * I;
+        const double* gu = gate_up + t * 2 * I;
         for (int64_t b = 0; b < I / B; ++b) {
             for (int64_t k = 0; k < B; ++k) {
                 int64_t j = b * B + k;
-                double g = dec16(gu[2 * j], dtype);
-                double u = dec16(gu[2 * j + 1], dtype);
-                h[k] = or_act(g, act) * u;
+                h[k] = or_act(gu[2 * j], act) * gu[2 * j + 1];
             }
             out_scales[t * (I / B) + b] =
                 or_quant_dynamic(h, B, out_fp8 + t * I + b * B);
         }
     }
+    return 0;
+}
+
+int oracle_gated_act_fp8(const uint16_t* gate_up, int act, uint8_t* out_fp8,
+                         float* out_scales, int64_t T, int64_t I, int dtype)
+{
+    double* gu = malloc(sizeof(double) * (size_t)(2 * I));
+    if (!gu)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t j = 0; j < 2 * I; ++j)
+            gu[j] = dec16(gate_up[t * 2 * I + j], dtype);
+        oracle_gated_act_fp8_f64(gu, act, out_fp8 + t * I,
+                                 out_scales + t * (I / 128), 1, I);
+    }
+    free(gu);
     return 0;
 }

@@ -91,6 +91,8 @@ int oracle_qkv_normrope_kvwrite(const uint16_t* qkv, const uint16_t* q_norm_w,
 
 int oracle_gated_act_fp8(const uint16_t* gate_up, int act, uint8_t* out_fp8,
                          float* out_scales, int64_t T, int64_t I, int dtype);
+int oracle_gated_act_fp8_f64(const double* gate_up, int act, uint8_t* out_fp8,
+                             float* out_scales, int64_t T, int64_t I);
 
 #ifdef __cplusplus
 }

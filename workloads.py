@@ -162,3 +162,28 @@ def chain_inputs(seed=102, layers=18, steps=10, T=10, H=1024, Hq=8, Hkv=1,
     out["dims"] = dict(layers=layers, steps=steps, T=T, H=H, Hq=Hq, Hkv=Hkv,
                        D=D, page_size=page_size)
     return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 GEMM fused with the gated activation (gate_up projection)
+# ---------------------------------------------------------------------------
+
+def e4m3_codes(x):
+    """float32 array -> OCP e4m3 codes through torch's float8_e4m3fn cast
+    (values must be within +-448)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def gemm_inputs(M, K, I, seed, scale_lo=0.5, scale_hi=2.0):
+    """A [M, K] and W [2I, K] as e4m3 codes of N(0,1) draws (x 32, well
+    inside the e4m3 range), with positive uniform block dequant scales:
+    a_scales [M, K/128] and w_scales [2I/128, K/128], each U(lo, hi) / 32 /
+    sqrt(K).  W rows interleave gate (2j) and up (2j+1) rows."""
+    rng = np.random.default_rng(seed)
+    a = e4m3_codes(normal(rng, (M, K)) * np.float32(32.0))
+    w = e4m3_codes(normal(rng, (2 * I, K)) * np.float32(32.0))
+    unit = np.float32(1.0 / 32.0 / np.sqrt(K))
+    a_s = rng.uniform(scale_lo, scale_hi, (M, K // 128)).astype(np.float32) * unit
+    w_s = rng.uniform(scale_lo, scale_hi, (2 * I // 128, K // 128)).astype(np.float32) * np.float32(1.0 / 32.0)
+    return {"a": a, "a_scales": a_s, "w": w, "w_scales": w_s}
