@@ -277,6 +277,9 @@ def main():
     # ---- standalone 10-token decode-boundary calls (median of 50) --------
     small = run_small(torch, fr, workloads, dev, stream)
 
+    # ---- gate_up FP8 GEMM fused with SwiGLU + block-128 FP8 --------------
+    gemm = run_gemm_act(torch, fr, workloads, dev, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
@@ -308,6 +311,7 @@ def main():
         "roofline": roofline,
         "chain": chain,
         "decode_t10": small,
+        "gemm_gated_act_fp8": gemm,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
@@ -374,6 +378,54 @@ def run_chain(torch, fr, workloads, HipGraph, dev, stream, replays):
         "us_per_op_p50": round(float(np.percentile(t, 50)) / nodes, 3),
         "eager_us_per_op": round(eager_us / nodes, 3),
     }
+
+
+PEAK_FP8_TFLOPS = 5000.0
+
+
+def run_gemm_act(torch, fr, workloads, dev, stream, reps=20):
+    """The gate_up projection of the prefill FFN fused with SwiGLU and the
+    block-128 FP8 output, at the Qwen3-VL 2B (hidden 2048, inter 6144) and 8B
+    (hidden 4096, inter 12288) shapes.  Weights rotate through >= 400 MB of
+    copies so every launch streams them from HBM."""
+    out = {}
+    for (M, K, I) in ((128, 2048, 6144), (192, 2048, 6144), (1024, 2048, 6144),
+                      (128, 4096, 12288)):
+        inp = workloads.gemm_inputs(M, K, I, 800 + M)
+        a, a_s = dev(inp["a"]), dev(inp["a_scales"])
+        w0, w_s = dev(inp["w"]), dev(inp["w_scales"])
+        nw = max(2, -(-(400 << 20) // w0.numel()))
+        ws = [w0] + [w0.clone() for _ in range(nw - 1)]
+        q = torch.empty((M, I), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((M, I // 128), dtype=torch.float32, device="cuda")
+
+        def f(i):
+            fr.fr_gemm_gated_act_fp8(a, a_s, ws[i % nw], w_s, fr.ACT_SWIGLU, q, sc,
+                                     M, K, I, stream=stream)
+        for i in range(3):
+            f(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(SPIN_CYCLES // 4)
+        e0.record(stream)
+        for i in range(reps):
+            f(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        flops = 2.0 * M * K * 2 * I
+        nbytes = 2 * I * K + M * K + 4 * M * K // 128 + 4 * (2 * I // 128) * (K // 128) \
+            + M * I + 4 * M * I // 128
+        out[f"M{M}_K{K}_I{I}"] = {
+            "us": round(us, 2),
+            "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+            "frac_of_fp8_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "bound": "mfma" if flops / (PEAK_FP8_TFLOPS * 1e12) > nbytes / (PEAK_HBM_GBS * 1e9) else "hbm",
+        }
+        del ws, w0
+    return out
 
 
 def run_small(torch, fr, workloads, dev, stream):

@@ -183,6 +183,32 @@ int fr_gated_act_fp8(const void* gate_up, int act, uint8_t* out_fp8,
                      float* out_scales, int64_t T, int64_t I, int dtype,
                      void* stream);
 
+/*
+ * (c') FP8 gate_up GEMM fused with the gated activation and block-128 FP8
+ *      [SM89 Phase 2 (gate_up GEMM + silu*up + per-token block-128 FP8 in
+ *      one launch, no [S, 2*inter] bf16 intermediate); FP third technique
+ *      (gate/up weight rows interleaved so one GEMM emits [g, u] pairs)]
+ *
+ *   acc[m,n] = sum_k dec(a[m,k]) a_scales[m,k/128] * dec(w[n,k]) w_scales[n/128,k/128]
+ *   h[m,j]   = act(acc[m,2j]) * acc[m,2j+1]     (fp32, not rounded in between)
+ *   out_scales[m,b] = max(max_j |h[m,j]| over block b of 128, 1e-10) / 448,
+ *   out_fp8[m,j] = E4M3(h[m,j] / out_scales[m, j/128])
+ *
+ *   a: [M,K] e4m3 codes, row-major; a_scales: [M, K/128] fp32 dequant scales
+ *     (the per-token block-128 format the FP8 producers write).
+ *   w: [2I,K] e4m3 codes, row 2j = gate row j, row 2j+1 = up row j;
+ *     w_scales: [2I/128, K/128] fp32 dequant scales of 128 x 128 blocks.
+ *   out_fp8: [M,I]; out_scales: [M, I/128].
+ *   Products are exact; sums are fp32 (matrix-core accumulation within a
+ *   128-wide K block, then scaled and added in fp32).
+ *   K % 128 == 0 (K <= 16384), I % 128 == 0; a, w, out_fp8 16-byte aligned,
+ *   scale arrays 4-byte aligned.  M == 0 launches nothing.
+ */
+int fr_gemm_gated_act_fp8(const uint8_t* a, const float* a_scales,
+                          const uint8_t* w, const float* w_scales, int act,
+                          uint8_t* out_fp8, float* out_scales, int64_t M,
+                          int64_t K, int64_t I, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fr_status_string(int status);
 

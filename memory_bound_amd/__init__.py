@@ -52,6 +52,8 @@ _SIGS = {
                                 _I32, _I32, _I32, _P, _I64, _I32, _I32, _I32,
                                 _INT, _P],
     "fr_gated_act_fp8": [_P, _INT, _P, _P, _I64, _I64, _INT, _P],
+    "fr_gemm_gated_act_fp8": [_P, _P, _P, _P, _INT, _P, _P, _I64, _I64, _I64,
+                              _P],
 }
 
 
@@ -153,3 +155,10 @@ def fr_gated_act_fp8(gate_up, act, out_fp8, out_scales, T, I, dtype,
     _check(lib.fr_gated_act_fp8(
         _ptr(gate_up), act, _ptr(out_fp8), _ptr(out_scales), T, I, dtype,
         _stream(stream)))
+
+
+def fr_gemm_gated_act_fp8(a, a_scales, w, w_scales, act, out_fp8, out_scales,
+                          M, K, I, stream=None):
+    _check(lib.fr_gemm_gated_act_fp8(
+        _ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales), act, _ptr(out_fp8),
+        _ptr(out_scales), M, K, I, _stream(stream)))

@@ -26,31 +26,7 @@
 
 namespace fr {
 
-enum { ACT_SWIGLU = 0, ACT_GEGLU_TANH = 1, ACT_SQRELU = 2 };
-
 constexpr int kActSteps = 8;   // block pairs per wave (bandwidth regime)
-
-template <int ACT>
-__device__ __forceinline__ float gate_act(float g) {
-    constexpr float kLog2e = 1.4426950408889634f;
-    if constexpr (ACT == ACT_SWIGLU) {
-        // g * sigmoid(g) = g / (1 + 2^(-g log2 e))
-        const float e = __builtin_amdgcn_exp2f(-g * kLog2e);
-        return g * __builtin_amdgcn_rcpf(1.0f + e);
-    } else if constexpr (ACT == ACT_GEGLU_TANH) {
-        // 0.5 g (1 + tanh z) = g * sigmoid(2z), z = sqrt(2/pi)(g + 0.044715 g^3);
-        // the sigmoid form has no cancellation for negative z.
-        constexpr float c1 = 2.0f * 0.7978845608028654f * kLog2e;
-        constexpr float c3 = 2.0f * 0.7978845608028654f * 0.044715f * kLog2e;
-        const float g2 = g * g;
-        const float arg = g * fmaf(c3, g2, c1);            // 2z log2 e
-        const float e = __builtin_amdgcn_exp2f(-arg);
-        return g * __builtin_amdgcn_rcpf(1.0f + e);
-    } else {
-        const float r = fmaxf(g, 0.0f);
-        return r * r;
-    }
-}
 
 // STEPS: block pairs per wave; NTL / NTS: non-temporal loads / stores.
 template <int DT, int ACT, int STEPS = kActSteps, bool NTL = true, bool NTS = true>
@@ -77,7 +53,6 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
         in[k] = NTL ? ld128_stream(row + off) : ld128(row + off);
     }
 
-    constexpr float kInv448 = 1.0f / 448.0f;
     float sc = 0.0f;                                     // lane i: scale of block i
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
@@ -91,11 +66,7 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
         // Block maximum over 32 lanes (all 64 lanes take part).
         m = group_reduce<16>(m, OpMax());
         m = rows_pair(m, OpMax());
-        const float amax = fmaxf(m, 1e-10f);
-        // s = amax / 448 correctly rounded: q0 = amax * (1/448), then one fma
-        // correction with the exact remainder amax - q0 * 448.
-        const float q0 = amax * kInv448;
-        const float s = fmaf(fmaf(-q0, 448.0f, amax), kInv448, q0);
+        const float s = div448(fmaxf(m, 1e-10f));        // correctly rounded
         const float inv = __builtin_amdgcn_rcpf(s);
         const int b = blk[k];
         if (b < a.nb) {

@@ -180,6 +180,32 @@ FR_EXPORT int fr_gated_act_fp8(const void* gate_up, int act, uint8_t* out_fp8,
     return launch_status(fr::launch_act(a, dtype, act, (hipStream_t)stream));
 }
 
+FR_EXPORT int fr_gemm_gated_act_fp8(const uint8_t* a, const float* a_scales,
+                                    const uint8_t* w, const float* w_scales,
+                                    int act, uint8_t* out_fp8, float* out_scales,
+                                    int64_t M, int64_t K, int64_t I, void* stream) {
+    if (M < 0 || K <= 0 || K % 128 != 0 || I <= 0 || I % 128 != 0) return FR_ERR_SHAPE;
+    if (K > 16384 || I > (1 << 20) || M > (1LL << 26)) return FR_ERR_UNSUPPORTED;
+    if (act != FR_ACT_SWIGLU && act != FR_ACT_GEGLU_TANH && act != FR_ACT_SQRELU)
+        return FR_ERR_MODE;
+    if (!a || !a_scales || !w || !w_scales || !out_fp8 || !out_scales) return FR_ERR_NULL;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(out_fp8)) return FR_ERR_ALIGN;
+    if (!aligned4(a_scales) || !aligned4(w_scales) || !aligned4(out_scales)) return FR_ERR_ALIGN;
+    if (M == 0) return FR_OK;
+    if (((M + 31) / 32) * (I / 128) > 0x7ffffff0LL) return FR_ERR_UNSUPPORTED;   // grid
+    fr::GemmActArgs g{};
+    g.A = a;
+    g.a_scales = a_scales;
+    g.B = w;
+    g.b_scales = w_scales;
+    g.out = out_fp8;
+    g.out_scales = out_scales;
+    g.M = (int)M;
+    g.K = (int)K;
+    g.I = (int)I;
+    return launch_status(fr::launch_gemm_act(g, act, (hipStream_t)stream));
+}
+
 FR_EXPORT const char* fr_status_string(int status) {
     switch (status) {
     case FR_OK: return "FR_OK";

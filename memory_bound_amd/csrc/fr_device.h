@@ -183,6 +183,42 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 }
 
 // ---------------------------------------------------------------------------
+// Gate activations (fp32): SiLU for SwiGLU, GELU with the tanh approximation
+// for GeGLU, squared ReLU.  v_exp_f32 / v_rcp_f32 are ~1 ulp.
+// ---------------------------------------------------------------------------
+enum { ACT_SWIGLU = 0, ACT_GEGLU_TANH = 1, ACT_SQRELU = 2 };
+
+template <int ACT>
+__device__ __forceinline__ float gate_act(float g) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    if constexpr (ACT == ACT_SWIGLU) {
+        // g * sigmoid(g) = g / (1 + 2^(-g log2 e))
+        const float e = __builtin_amdgcn_exp2f(-g * kLog2e);
+        return g * __builtin_amdgcn_rcpf(1.0f + e);
+    } else if constexpr (ACT == ACT_GEGLU_TANH) {
+        // 0.5 g (1 + tanh z) = g * sigmoid(2z), z = sqrt(2/pi)(g + 0.044715 g^3);
+        // the sigmoid form has no cancellation for negative z.
+        constexpr float c1 = 2.0f * 0.7978845608028654f * kLog2e;
+        constexpr float c3 = 2.0f * 0.7978845608028654f * 0.044715f * kLog2e;
+        const float g2 = g * g;
+        const float arg = g * fmaf(c3, g2, c1);            // 2z log2 e
+        const float e = __builtin_amdgcn_exp2f(-arg);
+        return g * __builtin_amdgcn_rcpf(1.0f + e);
+    } else {
+        const float r = fmaxf(g, 0.0f);
+        return r * r;
+    }
+}
+
+// Correctly rounded amax / 448: q0 = amax * (1/448), then one fma correction
+// with the exact remainder amax - q0 * 448.
+__device__ __forceinline__ float div448(float amax) {
+    constexpr float kInv448 = 1.0f / 448.0f;
+    const float q0 = amax * kInv448;
+    return fmaf(fmaf(-q0, 448.0f, amax), kInv448, q0);
+}
+
+// ---------------------------------------------------------------------------
 // Global memory access: 128-bit vector loads/stores.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 ld128(const void* p) {

@@ -65,8 +65,23 @@ struct ActArgs {
     int wpr;                // wavefronts per row
 };
 
+// FP8 block-scaled GEMM (gate_up projection) + gated activation + block-128 FP8.
+struct GemmActArgs {
+    const uint8_t* A;       // [M, K] e4m3
+    const float* a_scales;  // [M, K/128]
+    const uint8_t* B;       // [2I, K] e4m3, gate/up rows interleaved
+    const float* b_scales;  // [2I/128, K/128]
+    uint8_t* out;           // [M, I]
+    float* out_scales;      // [M, I/128]
+    int M, K, I;
+    int mt;                 // 32-row tiles
+    int tiles;              // mt * (I / 128)
+    int per_xcd;            // ceil(tiles / 8)
+};
+
 hipError_t launch_norm(const NormArgs& a, int dtype, bool adaptive, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int dtype, hipStream_t s);
 hipError_t launch_act(const ActArgs& a, int dtype, int act, hipStream_t s);
+hipError_t launch_gemm_act(const GemmActArgs& a, int act, hipStream_t s);
 
 }  // namespace fr

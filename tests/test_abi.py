@@ -27,8 +27,8 @@ def test_header_declares_the_four_ops_and_helpers():
     names = declared_functions()
     assert names == sorted([
         "fr_resid_rmsnorm_fp8", "fr_adarms_gate_res_fp8",
-        "fr_qkv_normrope_kvwrite", "fr_gated_act_fp8", "fr_status_string",
-        "fr_abi_version"])
+        "fr_qkv_normrope_kvwrite", "fr_gated_act_fp8", "fr_gemm_gated_act_fp8",
+        "fr_status_string", "fr_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -161,3 +161,19 @@ def test_binding_raises_on_bad_arguments():
     with pytest.raises(fr.FrError) as e:
         fr.fr_gated_act_fp8(A, 0, B, C, 10, 100, fr.BF16, stream=0)
     assert e.value.status == fr.FR_ERR_SHAPE
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, B, C, D_, 0, E, F, 10, 2048, 6144), fr.FR_ERR_NULL),
+    ((A, B, C, D_, 0, E, None, 10, 2048, 6144), fr.FR_ERR_NULL),
+    ((A, B, C, D_, 3, E, F, 10, 2048, 6144), fr.FR_ERR_MODE),
+    ((A, B, C, D_, 0, E, F, 10, 2000, 6144), fr.FR_ERR_SHAPE),
+    ((A, B, C, D_, 0, E, F, 10, 2048, 6100), fr.FR_ERR_SHAPE),
+    ((A, B, C, D_, 0, E, F, -1, 2048, 6144), fr.FR_ERR_SHAPE),
+    ((A, B, C, D_, 0, E, F, 10, 16384 + 128, 6144), fr.FR_ERR_UNSUPPORTED),
+    ((A + 8, B, C, D_, 0, E, F, 10, 2048, 6144), fr.FR_ERR_ALIGN),
+    ((A, B + 2, C, D_, 0, E, F, 10, 2048, 6144), fr.FR_ERR_ALIGN),
+    ((A, B, C, D_, 0, E, F, 0, 2048, 6144), fr.FR_OK),
+])
+def test_gemm_gated_act_validation(args, status):
+    assert fr.lib.fr_gemm_gated_act_fp8(*args, None) == status

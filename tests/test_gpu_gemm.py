@@ -1,0 +1,147 @@
+"""GPU parity of the FP8 gate_up GEMM fused with the gated activation and
+block-128 FP8 output, against the oracle (dequantise, float64 matmul,
+activation, block quantisation) on the same seeded codes and scales.
+
+Acceptance (derived from the arithmetic).  The gfx950 e4m3 matrix
+instruction sums its 64 exact products with a bounded error: measured on
+N(0,1)-scaled codes, |err| <= 2^-14.9 * sum|a b| for one instruction.  The
+kernel adds the two instructions of a 128-wide K block, scales the block
+sum and accumulates in fp32, so each accumulator carries
+|d acc| <= U * sum_k |a_k w_k| with U = 2^-13 (the measured bound with a
+margin of ~3.7x; fp32 terms are negligible beside it).  With S = sum|a w|
+(from the oracle's operands) and g, u the oracle's exact gate/up values:
+  E_h = |act'|max * dg * (|u| + du) + (|act(g)| + |act'|max * dg) * du,
+  dg = U * S_g, du = U * S_u, |act'| <= 1.2 for SiLU and GELU-tanh,
+  2 (|g| + dg) for ReLU^2.
+Every GPU code must lie in the e4m3 code interval of (h_o -+ E_h) / s_gpu,
+and every GPU scale within max_block(E_h) / 448 (+ 4 ulp) of the oracle's.
+The identical fraction is reported."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import announce, check_fp8, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fr():
+    import memory_bound_amd
+    return memory_bound_amd
+
+
+U_MFMA = 2.0 ** -13
+
+
+def _act(g, act):
+    if act == oracle.ACT_SWIGLU:
+        return g / (1.0 + np.exp(-g))
+    if act == oracle.ACT_GEGLU_TANH:
+        return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))
+    return np.maximum(g, 0.0) ** 2
+
+
+def _ord(c):
+    c = c.astype(np.int32)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def check_gemm_interval(q_g, s_g, q_o, s_o, inp, act):
+    """Interval parity (see the module docstring); returns (identical
+    fraction, max scale relative error)."""
+    A = oracle.dequant_blocks(inp["a"], inp["a_scales"], 1)
+    W = oracle.dequant_blocks(inp["w"], inp["w_scales"], 128)
+    acc = A @ W.T
+    S = np.abs(A) @ np.abs(W).T
+    g, u = acc[:, 0::2], acc[:, 1::2]
+    dg, du = U_MFMA * S[:, 0::2], U_MFMA * S[:, 1::2]
+    h = _act(g, act) * u
+    dmax = 2.0 * (np.abs(g) + dg) if act == oracle.ACT_SQRELU else 1.2
+    E = dmax * dg * (np.abs(u) + du) + (np.abs(_act(g, act)) + dmax * dg) * du
+    M, I = h.shape
+    s_g64 = s_g.astype(np.float64)
+    assert np.all(np.isfinite(s_g64)) and np.all(s_g64 > 0), "unwritten scales"
+    # scales: the block maximum moves by at most max(E) over the block
+    Eb = E.reshape(M, I // 128, 128).max(axis=2)
+    ulp = np.spacing(s_o.astype(np.float32)).astype(np.float64)
+    bad = np.abs(s_g64 - s_o) > Eb / 448.0 * 1.001 + 4 * ulp
+    assert not bad.any(), f"{bad.sum()} scales outside their bound"
+    # codes: inside the rounding interval of the perturbed exact value
+    sfull = np.repeat(s_g64, 128, axis=1)
+    lo = oracle.e4m3_encode_n((h - E) / sfull).reshape(M, I)
+    hi = oracle.e4m3_encode_n((h + E) / sfull).reshape(M, I)
+    og = _ord(q_g)
+    nan = (q_g & 0x7F) == 0x7F
+    assert not nan.any(), f"{nan.sum()} NaN / unwritten codes"
+    out = (og < _ord(lo)) | (og > _ord(hi))
+    if out.any():
+        i = np.argwhere(out)[0]
+        raise AssertionError(f"{out.sum()} codes outside their interval; first {tuple(i)}: "
+                             f"got {q_g[tuple(i)]:#04x} interval [{lo[tuple(i)]:#04x}, "
+                             f"{hi[tuple(i)]:#04x}] oracle {q_o[tuple(i)]:#04x}")
+    ident = float(np.mean((q_g == q_o) | (((q_g | q_o) & 0x7F) == 0)))
+    assert ident >= 0.99, f"only {ident:.6f} identical"
+    return ident, float((np.abs(s_g64 - s_o) / s_o).max())
+
+
+def run_gemm(fr, inp, act):
+    M, K = inp["a"].shape
+    I = inp["w"].shape[0] // 2
+    q = torch.full((M, I), 0x7F, dtype=torch.uint8, device="cuda")
+    sc = torch.full((M, I // 128), float("nan"), dtype=torch.float32, device="cuda")
+    fr.fr_gemm_gated_act_fp8(to_dev(inp["a"]), to_dev(inp["a_scales"]),
+                             to_dev(inp["w"]), to_dev(inp["w_scales"]), act, q, sc,
+                             M, K, I)
+    torch.cuda.synchronize()
+    return to_host(q, np.uint8), to_host(sc, np.float32)
+
+
+GEMM_CASES = [
+    # (M, K, I, act, seed)
+    (1, 128, 128, oracle.ACT_SWIGLU, 701),
+    (37, 256, 384, oracle.ACT_GEGLU_TANH, 702),          # ragged M, several tiles
+    (64, 2048, 256, oracle.ACT_SQRELU, 703),
+    (128, 2048, 6144, oracle.ACT_SWIGLU, 704),           # 2B gate_up, S=128
+    (192, 2048, 6144, oracle.ACT_SWIGLU, 705),           # 2B gate_up, S=192
+    (192, 2048, 6144, oracle.ACT_GEGLU_TANH, 705),
+    (128, 4096, 12288, oracle.ACT_SWIGLU, 706),          # 8B gate_up, S=128
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: f"M{c[0]}_K{c[1]}_I{c[2]}_act{c[3]}")
+def test_gemm_gated_act(fr, case):
+    M, K, I, act, seed = case
+    announce(f"gemm_gated_act M={M} K={K} I={I} act={act} seed={seed}")
+    inp = workloads.gemm_inputs(M, K, I, seed)
+    q_g, s_g = run_gemm(fr, inp, act)
+    q_o, s_o, _ = oracle.gemm_gated_act_fp8(inp["a"], inp["a_scales"], inp["w"],
+                                            inp["w_scales"], act)
+    ident, rel = check_gemm_interval(q_g, s_g, q_o, s_o, inp, act)
+    announce(f"  fp8 identical {ident:.6f}, scale max rel err {rel:.2e}")
+
+
+def test_gemm_worked_example(fr):
+    announce("gemm worked example")
+    K, I = 128, 128
+    a = np.full((1, K), 0x38, dtype=np.uint8)
+    w = np.zeros((2 * I, K), dtype=np.uint8)
+    w[0::2, 0] = 0x38
+    for j in range(I):
+        w[2 * j + 1, : [1, 2, 4, 8][j % 4]] = 0x38
+    inp = {"a": a, "a_scales": np.ones((1, 1), np.float32), "w": w,
+           "w_scales": np.ones((2, 1), np.float32)}
+    q, s = run_gemm(fr, inp, oracle.ACT_SWIGLU)
+    assert list(q[0, :8]) == [0x66, 0x6E, 0x76, 0x7E] * 2
+
+
+def test_gemm_determinism(fr):
+    announce("gemm determinism x3")
+    inp = workloads.gemm_inputs(96, 1024, 1024, 707)
+    first = run_gemm(fr, inp, oracle.ACT_SWIGLU)
+    for _ in range(2):
+        again = run_gemm(fr, inp, oracle.ACT_SWIGLU)
+        assert np.array_equal(first[0], again[0])
+        assert np.array_equal(first[1].view(np.uint32), again[1].view(np.uint32))
