@@ -386,14 +386,19 @@ PEAK_FP8_TFLOPS = 5000.0
 def run_gemm_act(torch, fr, workloads, dev, stream, reps=20):
     """The gate_up projection of the prefill FFN fused with SwiGLU and the
     block-128 FP8 output, at the Qwen3-VL 2B (hidden 2048, inter 6144) and 8B
-    (hidden 4096, inter 12288) shapes.  Weights rotate through >= 400 MB of
-    copies so every launch streams them from HBM."""
+    (hidden 4096, inter 12288) shapes.  Weights are packed once (outside the
+    timing) and rotate through >= 400 MB of copies so every launch streams
+    them from HBM."""
     out = {}
     for (M, K, I) in ((128, 2048, 6144), (192, 2048, 6144), (1024, 2048, 6144),
-                      (128, 4096, 12288)):
+                      (128, 4096, 12288), (4096, 4096, 12288)):
         inp = workloads.gemm_inputs(M, K, I, 800 + M)
         a, a_s = dev(inp["a"]), dev(inp["a_scales"])
-        w0, w_s = dev(inp["w"]), dev(inp["w_scales"])
+        w_raw, w_s = dev(inp["w"]), dev(inp["w_scales"])
+        w0 = torch.empty_like(w_raw)
+        fr.fr_gemm_pack_weights(w_raw, w0, 2 * I, K, stream=stream)
+        torch.cuda.synchronize()
+        del w_raw
         nw = max(2, -(-(400 << 20) // w0.numel()))
         ws = [w0] + [w0.clone() for _ in range(nw - 1)]
         q = torch.empty((M, I), dtype=torch.uint8, device="cuda")

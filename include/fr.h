@@ -196,18 +196,36 @@ int fr_gated_act_fp8(const void* gate_up, int act, uint8_t* out_fp8,
  *
  *   a: [M,K] e4m3 codes, row-major; a_scales: [M, K/128] fp32 dequant scales
  *     (the per-token block-128 format the FP8 producers write).
- *   w: [2I,K] e4m3 codes, row 2j = gate row j, row 2j+1 = up row j;
- *     w_scales: [2I/128, K/128] fp32 dequant scales of 128 x 128 blocks.
+ *   w_packed: the [2I,K] e4m3 weight (row 2j = gate row j, row 2j+1 = up
+ *     row j) in the layout fr_gemm_pack_weights writes (packed once, at
+ *     load time); w_scales: [2I/128, K/128] fp32 dequant scales of 128 x 128
+ *     blocks of the unpacked weight.
  *   out_fp8: [M,I]; out_scales: [M, I/128].
  *   Products are exact; sums are fp32 (matrix-core accumulation within a
  *   128-wide K block, then scaled and added in fp32).
- *   K % 128 == 0 (K <= 16384), I % 128 == 0; a, w, out_fp8 16-byte aligned,
- *   scale arrays 4-byte aligned.  M == 0 launches nothing.
+ *   K % 128 == 0 (K <= 16384), I % 128 == 0; a, w_packed, out_fp8 16-byte
+ *   aligned, scale arrays 4-byte aligned.  M == 0 launches nothing.
  */
 int fr_gemm_gated_act_fp8(const uint8_t* a, const float* a_scales,
-                          const uint8_t* w, const float* w_scales, int act,
+                          const uint8_t* w_packed, const float* w_scales, int act,
                           uint8_t* out_fp8, float* out_scales, int64_t M,
                           int64_t K, int64_t I, void* stream);
+
+/*
+ * Weight packing for fr_gemm_gated_act_fp8 (a byte permutation, no
+ * arithmetic).  w: [N,K] e4m3 codes, row-major; w_packed: N*K bytes, must
+ * not overlap w.  Unit u (16 bytes at w_packed + 16u) holds, with
+ *   lane = u % 64, c = (u / 64) % 4, kb = (u / 256) % (K/128),
+ *   G = u / (256 * K/128), row = 32 G + lane % 32,
+ *   off = 64 (c / 2) + 32 (lane / 32) + 16 (c % 2),
+ * the bytes w[row, 128 kb + off .. 128 kb + off + 15]: the operand
+ * fragments of one 32-row group and one 128-wide K block form 4 KB of
+ * consecutive bytes, so every fragment load of the GEMM reads whole cache
+ * lines.  N % 32 == 0, K % 128 == 0 (K <= 16384); both pointers 16-byte
+ * aligned.  N == 0 launches nothing.
+ */
+int fr_gemm_pack_weights(const uint8_t* w, uint8_t* w_packed, int64_t N,
+                         int64_t K, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fr_status_string(int status);

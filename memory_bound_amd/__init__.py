@@ -54,6 +54,7 @@ _SIGS = {
     "fr_gated_act_fp8": [_P, _INT, _P, _P, _I64, _I64, _INT, _P],
     "fr_gemm_gated_act_fp8": [_P, _P, _P, _P, _INT, _P, _P, _I64, _I64, _I64,
                               _P],
+    "fr_gemm_pack_weights": [_P, _P, _I64, _I64, _P],
 }
 
 
@@ -157,8 +158,13 @@ def fr_gated_act_fp8(gate_up, act, out_fp8, out_scales, T, I, dtype,
         _stream(stream)))
 
 
-def fr_gemm_gated_act_fp8(a, a_scales, w, w_scales, act, out_fp8, out_scales,
-                          M, K, I, stream=None):
+def fr_gemm_gated_act_fp8(a, a_scales, w_packed, w_scales, act, out_fp8,
+                          out_scales, M, K, I, stream=None):
     _check(lib.fr_gemm_gated_act_fp8(
-        _ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales), act, _ptr(out_fp8),
-        _ptr(out_scales), M, K, I, _stream(stream)))
+        _ptr(a), _ptr(a_scales), _ptr(w_packed), _ptr(w_scales), act,
+        _ptr(out_fp8), _ptr(out_scales), M, K, I, _stream(stream)))
+
+
+def fr_gemm_pack_weights(w, w_packed, N, K, stream=None):
+    _check(lib.fr_gemm_pack_weights(_ptr(w), _ptr(w_packed), N, K,
+                                    _stream(stream)))

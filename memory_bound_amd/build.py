@@ -1,6 +1,8 @@
 """Compile the HIP library libfrhip.so in-tree for gfx950.
 
-    python -m memory_bound_amd.build
+    python memory_bound_amd/build.py
+
+(run by path: importing the package loads the library being rebuilt)
 """
 import os
 import subprocess
@@ -17,6 +19,9 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the GEMM's per-block scale fold
+    # then reads them without accumulator-register copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-result",
 ]
 

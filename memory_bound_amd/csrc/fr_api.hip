@@ -181,22 +181,22 @@ FR_EXPORT int fr_gated_act_fp8(const void* gate_up, int act, uint8_t* out_fp8,
 }
 
 FR_EXPORT int fr_gemm_gated_act_fp8(const uint8_t* a, const float* a_scales,
-                                    const uint8_t* w, const float* w_scales,
+                                    const uint8_t* w_packed, const float* w_scales,
                                     int act, uint8_t* out_fp8, float* out_scales,
                                     int64_t M, int64_t K, int64_t I, void* stream) {
     if (M < 0 || K <= 0 || K % 128 != 0 || I <= 0 || I % 128 != 0) return FR_ERR_SHAPE;
     if (K > 16384 || I > (1 << 20) || M > (1LL << 26)) return FR_ERR_UNSUPPORTED;
     if (act != FR_ACT_SWIGLU && act != FR_ACT_GEGLU_TANH && act != FR_ACT_SQRELU)
         return FR_ERR_MODE;
-    if (!a || !a_scales || !w || !w_scales || !out_fp8 || !out_scales) return FR_ERR_NULL;
-    if (!aligned16(a) || !aligned16(w) || !aligned16(out_fp8)) return FR_ERR_ALIGN;
+    if (!a || !a_scales || !w_packed || !w_scales || !out_fp8 || !out_scales) return FR_ERR_NULL;
+    if (!aligned16(a) || !aligned16(w_packed) || !aligned16(out_fp8)) return FR_ERR_ALIGN;
     if (!aligned4(a_scales) || !aligned4(w_scales) || !aligned4(out_scales)) return FR_ERR_ALIGN;
     if (M == 0) return FR_OK;
     if (((M + 31) / 32) * (I / 128) > 0x7ffffff0LL) return FR_ERR_UNSUPPORTED;   // grid
     fr::GemmActArgs g{};
     g.A = a;
     g.a_scales = a_scales;
-    g.B = w;
+    g.B = w_packed;
     g.b_scales = w_scales;
     g.out = out_fp8;
     g.out_scales = out_scales;
@@ -204,6 +204,21 @@ FR_EXPORT int fr_gemm_gated_act_fp8(const uint8_t* a, const float* a_scales,
     g.K = (int)K;
     g.I = (int)I;
     return launch_status(fr::launch_gemm_act(g, act, (hipStream_t)stream));
+}
+
+FR_EXPORT int fr_gemm_pack_weights(const uint8_t* w, uint8_t* w_packed, int64_t N,
+                                   int64_t K, void* stream) {
+    if (N < 0 || N % 32 != 0 || K <= 0 || K % 128 != 0) return FR_ERR_SHAPE;
+    if (K > 16384 || N > (1LL << 22)) return FR_ERR_UNSUPPORTED;
+    if (!w || !w_packed) return FR_ERR_NULL;
+    if (!aligned16(w) || !aligned16(w_packed)) return FR_ERR_ALIGN;
+    if (N == 0) return FR_OK;
+    fr::PackArgs p{};
+    p.w = w;
+    p.wp = w_packed;
+    p.N = N;
+    p.K = K;
+    return launch_status(fr::launch_pack_w(p, (hipStream_t)stream));
 }
 
 FR_EXPORT const char* fr_status_string(int status) {

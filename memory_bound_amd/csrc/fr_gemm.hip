@@ -1,5 +1,6 @@
 // fr_gemm.hip -- FP8 block-scaled gate_up GEMM fused with the gated
-// activation and per-token block-128 FP8 output, on the gfx950 matrix cores.
+// activation and per-token block-128 FP8 output, on the gfx950 matrix cores,
+// and the one-time weight packing it reads.
 //
 // Definitions: "sm89 prefill FFN megakernel" issue, Phase 2 (gate_up GEMM +
 // silu * up + per-token block-128 FP8 quantisation in one launch, removing
@@ -10,23 +11,38 @@
 //
 // C[m, n] = sum_k A[m, k] a_s[m, k/128] * W[n, k] w_s[n/128, k/128] with A,
 // W e4m3 and fp32 dequant scales; n = 2j is gate output j, n = 2j+1 its up
-// partner.  Each workgroup (4 waves) owns a tile of 32 rows x 256 columns,
-// i.e. exactly one 128-output block of the result, so the block maximum
-// never leaves the workgroup.  Wave w computes columns [64w, 64w+64) as two
-// 32x32 tiles with v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, unit MX
-// scales): per 128-wide K block it runs 2 x 2 MFMAs into a fresh fp32
-// partial, then folds the partial into the accumulator times
-// a_s(row) * w_s, with the activation scale panel of the tile in LDS.  The
+// partner.  Each workgroup (4 waves) owns a tile of 32 RG rows x 256
+// columns, i.e. exactly one 128-output block of the result per row, so the
+// block maximum never leaves the workgroup.  Wave w computes columns
+// [64w, 64w+64) of all the tile's rows as 2 RG tiles of 32x32 with
+// v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, unit MX scales): per
+// 128-wide K block it runs two MFMAs per tile into a fresh fp32 partial,
+// then folds the partial into the accumulator times a_s(row) * w_s.  The
 // instruction's own sum of 64 products is not exact (about 15 bits relative
 // to the sum of magnitudes on MI355X), so partials are promoted to fp32 at
-// every 128-wide K block.  Operand fragments come straight from global
-// memory (lane l: row l % 32, 32 consecutive K bytes at 32 * (l / 32)),
-// DEPTH K blocks ahead of the MFMAs.
-// Epilogue: the fp32 tile goes through LDS, then each wave takes 8 rows:
-// every lane reads (g, u, g, u) for two outputs, applies the activation,
-// and the wave reduces the block maximum and writes 128 codes and a scale.
-// Tiles are ordered so that each XCD (which serves blocks b with b % 8
-// fixed) walks a contiguous range of tiles, and the 32-row tiles of one
+// every 128-wide K block.
+//
+// Operand traffic.  An MFMA fragment puts row (l % 32) in lane l, so a
+// fragment loaded straight from a row-major matrix touches 32 cache lines
+// per instruction.  The weights are therefore packed once
+// (fr_gemm_pack_weights) so that every fragment load of a wave reads 1 KB
+// of consecutive bytes, DEPTH K blocks ahead of the MFMAs, into registers.
+// The activation tile is shared by the 4 waves: each wave fetches one
+// quarter of every K block (DEPTH blocks ahead, in registers) and writes it
+// to a double-buffered LDS stage laid out in fragment order, so the
+// fragment reads are conflict-free; one barrier per K block.  (Direct
+// global->LDS loads would save the register hop, but the compiler then
+// waits for every outstanding load before each LDS read.)  The scale
+// panels of the tile are staged in LDS before the loop.  Measured on
+// MI355X, this layout runs 1.5x (128 tokens) to 3x (4096 tokens) faster
+// than fragments loaded straight from the row-major weight.
+//
+// Epilogue: a gate column and its up partner sit in adjacent lanes; a DPP
+// pair swap gives both lanes act(g) * u.  Row maxima are reduced across
+// the wave's 32 outputs with DPP, combined across the 4 waves in LDS, and
+// the codes go through LDS so each output row leaves as 128 contiguous
+// bytes.  Tiles are ordered so that each XCD (which serves blocks b with
+// b % 8 fixed) walks a contiguous range of tiles: the row tiles of one
 // 256-column weight panel run together on one XCD and share its L2.
 #include "fr_device.h"
 #include "fr_launch.h"
@@ -36,11 +52,10 @@ namespace fr {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kGemmMaxKB = 128;   // K <= 16384
-constexpr int kGemmDepth = 2;      // K blocks in flight per wave
+constexpr int kGemmMaxKB = 128;     // K <= 16384
+constexpr int kGemmPanel = 4096;    // rows x K blocks of the staged a_s panel
 
-__device__ __forceinline__ i32x8 ld256(const uint8_t* p) {
-    const u32x4 lo = ld128(p), hi = ld128(p + 16);
+__device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
     i32x8 r;
     r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
     r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
@@ -52,165 +67,252 @@ __device__ __forceinline__ f32x16 mma_e4m3(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// DEPTH: K blocks whose operand fragments are in flight per wave (a ring of
-// registers; the loop is unrolled by DEPTH so every slot index is static).
-// The loop body is one basic block that issues no global load other than
-// the ring refills, so the wait for slot d never covers the loads of later
-// slots.  K is padded to a multiple of DEPTH with blocks whose scales are
-// zero (their operands re-read the last real block, so they stay finite).
-template <int ACT, int DEPTH>
+__device__ __forceinline__ u32x4 lds128(const uint8_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Byte offset, within a 128-wide K block, of the 16 bytes that chunk c
+// (0..3) gives lane half kh: chunks 2h and 2h+1 form the 32-byte fragment
+// of the h-th 64-wide MFMA step.
+__device__ __forceinline__ int chunk_koff(int c, int kh) {
+    return 64 * (c >> 1) + 32 * kh + 16 * (c & 1);
+}
+
+// RG: 32-row groups per tile (32 RG x K/128 <= kGemmPanel); DEPTH: K blocks
+// in flight per wave (even, so the LDS stage of a block is static).
+template <int ACT, int RG, int DEPTH>
 __global__ __launch_bounds__(256) void k_gemm_act(GemmActArgs a) {
-    static_assert(kGemmMaxKB % DEPTH == 0 && 2 * kGemmMaxKB == 256, "padding");
-    __shared__ float tile[32 * 256];
-    __shared__ float4 asc4[kGemmMaxKB * 8];              // [kb][row / 4], 4 rows
-    __shared__ float bsc[2 * kGemmMaxKB];                // [128-col block][kb]
+    constexpr int ROWS = 32 * RG;
+    static_assert(DEPTH % 2 == 0, "stage parity must be static");
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2 * RG * 4096];
+    __shared__ __attribute__((aligned(16))) float asp[kGemmPanel];          // [kb][row]
+    __shared__ __attribute__((aligned(16))) float bsp[2 * kGemmMaxKB];     // [block][kb]
+    __shared__ __attribute__((aligned(16))) float red[ROWS * 4];           // [row][wave]
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = threadIdx.x >> 6;                      // column quarter
     const int L = (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
     if (L >= a.tiles) return;                            // whole workgroup exits
     const int n_tile = L / a.mt;
     const int m_tile = L - n_tile * a.mt;
-    const int m0 = m_tile * 32;
-    const int n0 = n_tile * 256;
+    const int m0 = m_tile * ROWS;
     const int KB = a.K >> 7;
-    const int KBp = (KB + DEPTH - 1) / DEPTH * DEPTH;
+    const int KBp = (KB + DEPTH - 1) / DEPTH * DEPTH;    // padded: scale 0
+    const int rl = lane & 31;
+    const int kh = lane >> 5;
 
-    // Scale panels of the tile: activation scales of its 32 rows (rows past
-    // M repeat row M-1), stored transposed so that one 16-byte LDS read gives
-    // the 4 consecutive rows that accumulator registers 4q..4q+3 of a lane
-    // hold; weight scales of its two 128-column blocks.  Padding blocks get
-    // zero.  Loaded to registers first so that the LDS stores below wait
-    // only for these loads, not for the operand ring issued after them.
-    float sv[16];
+    // Scale panels, loaded to registers before the operand loads so that
+    // their LDS stores below wait for these loads only: a_s of the tile's
+    // rows (rows past M repeat row M-1) as [kb][row], so one 16-byte read
+    // gives the 4 consecutive rows held by accumulator registers 4q..4q+3;
+    // w_s of the two 128-column blocks (2 consecutive rows of w_s).
+    constexpr int PJ = kGemmPanel / 256;
+    float sv[PJ];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {                       // 16 * 256 = 32 * kGemmMaxKB
-        const int i = threadIdx.x + 256 * j;             // = kb * 32 + row
-        const int kb = i >> 5;
-        const int m = min(m0 + (i & 31), a.M - 1);
-        sv[j] = a.a_scales[(int64_t)m * KB + min(kb, KB - 1)];
+    for (int j = 0; j < PJ; ++j) {
+        const int e = min((int)threadIdx.x + 256 * j, ROWS * KB - 1);
+        const int kb = e / ROWS, row = e - kb * ROWS;
+        sv[j] = a.a_scales[(int64_t)min(m0 + row, a.M - 1) * KB + kb];
     }
-    float bv;
-    {
-        const int t = min((int)threadIdx.x, 2 * KBp - 1);
-        const int j = t / KBp, kb = t - j * KBp;
-        bv = a.b_scales[(int64_t)((n0 >> 7) + j) * KB + min(kb, KB - 1)];
-    }
-    __builtin_amdgcn_sched_barrier(0);                   // scale loads first
+    const int tb = min((int)threadIdx.x, 2 * KB - 1);
+    const float bv = a.b_scales[(int64_t)(2 * n_tile) * KB + tb];
+    __builtin_amdgcn_sched_barrier(0);
 
-    const int rl = lane & 31;                            // fragment row / column
-    const int kh = lane >> 5;                            // K half of a 64-wide step
-    const uint8_t* ap = a.A + (int64_t)min(m0 + rl, a.M - 1) * a.K + kh * 32;
-    const uint8_t* bp0 = a.B + (int64_t)(n0 + 64 * w + rl) * a.K + kh * 32;
-    const uint8_t* bp1 = bp0 + (int64_t)32 * a.K;
-
-    // operand ring: slot d holds K block kb with kb % DEPTH == d
-    i32x8 ra0[DEPTH], ra1[DEPTH], rb00[DEPTH], rb01[DEPTH], rb10[DEPTH], rb11[DEPTH];
+    // Activation chunk of this wave: chunk w of every row group.
+    const uint8_t* ag[RG];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-        const int o = min(d, KB - 1) * 128;
-        ra0[d] = ld256(ap + o);
-        ra1[d] = ld256(ap + o + 64);
-        rb00[d] = ld256(bp0 + o);
-        rb01[d] = ld256(bp0 + o + 64);
-        rb10[d] = ld256(bp1 + o);
-        rb11[d] = ld256(bp1 + o + 64);
-    }
+    for (int g = 0; g < RG; ++g)
+        ag[g] = a.A + (int64_t)min(m0 + 32 * g + rl, a.M - 1) * a.K + chunk_koff(w, kh);
+    // Packed weights: the wave's two 32-column groups, 4 KB per K block each.
+    const uint8_t* bq0 = a.B + (int64_t)(8 * n_tile + 2 * w) * KB * 4096 + lane * 16;
+    const uint8_t* bq1 = bq0 + (int64_t)KB * 4096;
 
-    float* ascf = reinterpret_cast<float*>(asc4);
+    u32x4 ra[DEPTH][RG];
+    i32x8 rb00[DEPTH], rb01[DEPTH], rb10[DEPTH], rb11[DEPTH];   // [group][step]
+    auto issue = [&](int d, int kb) {
+        const int o = kb * 4096;
+        rb00[d] = join(ld128(bq0 + o), ld128(bq0 + o + 1024));
+        rb01[d] = join(ld128(bq0 + o + 2048), ld128(bq0 + o + 3072));
+        rb10[d] = join(ld128(bq1 + o), ld128(bq1 + o + 1024));
+        rb11[d] = join(ld128(bq1 + o + 2048), ld128(bq1 + o + 3072));
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int i = threadIdx.x + 256 * j;
-        ascf[i] = (i >> 5) < KB ? sv[j] : 0.0f;
-    }
-    {
-        const int t = min((int)threadIdx.x, 2 * KBp - 1);
-        bsc[threadIdx.x] = t - t / KBp * KBp < KB ? bv : 0.0f;   // >= 2 KBp: unused
-    }
-    __syncthreads();
-    const float* bs = bsc + (w >> 1) * KBp;
+        for (int g = 0; g < RG; ++g) ra[d][g] = ld128(ag[g] + kb * 128);
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(d, min(d, KB - 1));
+    __builtin_amdgcn_sched_barrier(0);                   // operand loads before the stores
 
-    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int j = 0; j < PJ; ++j) asp[threadIdx.x + 256 * j] = sv[j];
+    bsp[threadIdx.x] = bv;                               // entries >= 2 KB unused
+
+    f32x16 acc[RG][2];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) acc[g][0] = acc[g][1] = f32x16{};
+    const float* bsw = bsp + (w >> 1) * KB;
     for (int kb0 = 0; kb0 < KBp; kb0 += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int kb = kb0 + d;
-            float4 sa[4];
+            uint8_t* st = stage + (d & 1) * RG * 4096 + lane * 16;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sa[q] = asc4[kb * 8 + 2 * q + kh];
-            const float bk = bs[kb];
-            f32x16 p0 = {}, p1 = {};
-            p0 = mma_e4m3(ra0[d], rb00[d], p0);
-            p1 = mma_e4m3(ra0[d], rb10[d], p1);
-            p0 = mma_e4m3(ra1[d], rb01[d], p0);
-            p1 = mma_e4m3(ra1[d], rb11[d], p1);
-            // refill the slot (past the end: re-read the last block, a cache
-            // hit, so the loop body stays free of branches)
-            const int o = min(kb + DEPTH, KB - 1) * 128;
-            ra0[d] = ld256(ap + o);
-            ra1[d] = ld256(ap + o + 64);
-            rb00[d] = ld256(bp0 + o);
-            rb01[d] = ld256(bp0 + o + 64);
-            rb10[d] = ld256(bp1 + o);
-            rb11[d] = ld256(bp1 + o + 64);
+            for (int g = 0; g < RG; ++g)
+                *reinterpret_cast<u32x4*>(st + (g * 4 + w) * 1024) = ra[d][g];
+            __syncthreads();                             // stage (and panels) complete
+            i32x8 fa[RG][2];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float f[4] = {sa[q].x * bk, sa[q].y * bk, sa[q].z * bk, sa[q].w * bk};
+            for (int g = 0; g < RG; ++g) {
+                fa[g][0] = join(lds128(st + (g * 4 + 0) * 1024), lds128(st + (g * 4 + 1) * 1024));
+                fa[g][1] = join(lds128(st + (g * 4 + 2) * 1024), lds128(st + (g * 4 + 3) * 1024));
+            }
+            const int kbc = min(kb, KB - 1);
+            const float bk = kb < KB ? bsw[kbc] : 0.0f;  // padding blocks add 0
+            f32x16 p[RG][2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc0[4 * q + e] = fmaf(p0[4 * q + e], f[e], acc0[4 * q + e]);
-                    acc1[4 * q + e] = fmaf(p1[4 * q + e], f[e], acc1[4 * q + e]);
+            for (int g = 0; g < RG; ++g) {
+                p[g][0] = mma_e4m3(fa[g][0], rb00[d], f32x16{});
+                p[g][1] = mma_e4m3(fa[g][0], rb10[d], f32x16{});
+                p[g][0] = mma_e4m3(fa[g][1], rb01[d], p[g][0]);
+                p[g][1] = mma_e4m3(fa[g][1], rb11[d], p[g][1]);
+            }
+            // refill the slot (past the end: re-read the last block, never used)
+            issue(d, min(kb + DEPTH, KB - 1));
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 sa = *reinterpret_cast<const float4*>(
+                        asp + kbc * ROWS + 32 * g + 8 * q + 4 * kh);
+                    const float f[4] = {sa.x * bk, sa.y * bk, sa.z * bk, sa.w * bk};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[g][0][4 * q + e] = fmaf(p[g][0][4 * q + e], f[e], acc[g][0][4 * q + e]);
+                        acc[g][1][4 * q + e] = fmaf(p[g][1][4 * q + e], f[e], acc[g][1][4 * q + e]);
+                    }
                 }
             }
+            // Keep K blocks in order: block kb's MFMAs and fold must not
+            // drift behind the barrier of the next block (that would halve
+            // the prefetch distance).  An empty volatile asm that takes the
+            // accumulators pins the fold here.
+#pragma unroll
+            for (int g = 0; g < RG; ++g) asm volatile("" : "+v"(acc[g][0]), "+v"(acc[g][1]));
         }
     }
 
-    // epilogue: tile to LDS, then one row per step per wave
+    // Epilogue.  Column 64w + 32t + rl of the tile is gate (rl even) or up
+    // (rl odd) of output 32w + 16t + rl/2 of the block.
+    {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * kh + (r & 3);
-        tile[row * 256 + 64 * w + rl] = acc0[r];
-        tile[row * 256 + 64 * w + 32 + rl] = acc1[r];
+        for (int g = 0; g < RG; ++g) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float v = acc[g][t][r];
+                    const float pv = dpp_f<DPP_PAIR>(v);
+                    const float gv = (rl & 1) ? pv : v, uv = (rl & 1) ? v : pv;
+                    acc[g][t][r] = gate_act<ACT>(gv) * uv;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float m = fmaxf(fabsf(acc[g][0][r]), fabsf(acc[g][1][r]));
+                m = group_reduce<16>(m, OpMax());
+                m = rows_pair(m, OpMax());               // over the 32 lanes of kh
+                if (rl == 0) red[(32 * g + 8 * (r >> 2) + 4 * kh + (r & 3)) * 4 + w] = m;
+            }
+        }
+    }
+    __syncthreads();                                     // stages are reused below
+    uint8_t* otile = stage;                              // [row][128] codes
+    const int nbo = a.I >> 7;
+    {
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * g + 8 * (r >> 2) + 4 * kh + (r & 3);
+                const float4 mm = *reinterpret_cast<const float4*>(red + row * 4);
+                const float mx = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
+                const float s = div448(fmaxf(mx, 1e-10f));   // correctly rounded
+                const float inv = __builtin_amdgcn_rcpf(s);
+                // |h * inv| <= 448 (1 + 3 ulp) < 464: no clamp needed
+                const int q = __builtin_amdgcn_cvt_pk_fp8_f32(acc[g][0][r] * inv,
+                                                              acc[g][1][r] * inv, 0, false);
+                if (!(rl & 1)) {
+                    otile[row * 128 + 32 * w + (rl >> 1)] = (uint8_t)q;
+                    otile[row * 128 + 32 * w + 16 + (rl >> 1)] = (uint8_t)(q >> 8);
+                }
+                if (w == 0 && rl == 0 && m0 + row < a.M)
+                    a.out_scales[(int64_t)(m0 + row) * nbo + n_tile] = s;
+            }
+        }
     }
     __syncthreads();
-#pragma unroll 1
-    for (int i = 0; i < 8; ++i) {
-        const int row = w * 8 + i;
-        const int m = m0 + row;
-        const float4 v = *reinterpret_cast<const float4*>(&tile[row * 256 + 4 * lane]);
-        const float h0 = gate_act<ACT>(v.x) * v.y;
-        const float h1 = gate_act<ACT>(v.z) * v.w;
-        const float mx = wave_reduce(fmaxf(fabsf(h0), fabsf(h1)), OpMax());
-        const float s = div448(fmaxf(mx, 1e-10f));
-        const float inv = __builtin_amdgcn_rcpf(s);
-        if (m < a.M) {
-            // |h * inv| <= 448 (1 + 3 ulp) < 464: no clamp needed
-            const int q = __builtin_amdgcn_cvt_pk_fp8_f32(h0 * inv, h1 * inv, 0, false);
-            *reinterpret_cast<uint16_t*>(a.out + (int64_t)m * a.I + n_tile * 128 + 2 * lane) =
-                (uint16_t)q;
-            if (lane == 0) a.out_scales[(int64_t)m * (a.I >> 7) + n_tile] = s;
+    {
+#pragma unroll
+        for (int i = 0; i < RG; ++i) {
+            const int row = (w + 4 * i) * 8 + (lane >> 3);
+            if (m0 + row < a.M)
+                st128(a.out + (int64_t)(m0 + row) * a.I + n_tile * 128 + (lane & 7) * 16,
+                      lds128(otile + row * 128 + (lane & 7) * 16));
         }
     }
 }
 
-template <int DEPTH>
-static hipError_t launch_gemm_depth(const GemmActArgs& in, int act, hipStream_t s) {
+template <int RG, int DEPTH>
+static hipError_t launch_gemm_cfg(const GemmActArgs& in, int act, hipStream_t s) {
     GemmActArgs a = in;
-    a.mt = (a.M + 31) / 32;
+    a.mt = (a.M + 32 * RG - 1) / (32 * RG);
     a.tiles = a.mt * (a.I / 128);
     a.per_xcd = (a.tiles + 7) / 8;
     const void* fn;
     switch (act) {
-    case ACT_SWIGLU: fn = (const void*)k_gemm_act<ACT_SWIGLU, DEPTH>; break;
-    case ACT_GEGLU_TANH: fn = (const void*)k_gemm_act<ACT_GEGLU_TANH, DEPTH>; break;
-    default: fn = (const void*)k_gemm_act<ACT_SQRELU, DEPTH>; break;
+    case ACT_SWIGLU: fn = (const void*)k_gemm_act<ACT_SWIGLU, RG, DEPTH>; break;
+    case ACT_GEGLU_TANH: fn = (const void*)k_gemm_act<ACT_GEGLU_TANH, RG, DEPTH>; break;
+    default: fn = (const void*)k_gemm_act<ACT_SQRELU, RG, DEPTH>; break;
     }
     void* args[] = {&a};
     return hipLaunchKernel(fn, dim3((unsigned)(8 * a.per_xcd)), dim3(256), args, 0, s);
 }
 
+// Row groups per tile.  Measured on MI355X (hidden 2048 / 4096, inter 6144 /
+// 12288, 128 to 4096 tokens): 64-row tiles win once they still give every CU
+// a tile, 32-row tiles otherwise; 128-row tiles and 4 K blocks in flight
+// were never faster.
 hipError_t launch_gemm_act(const GemmActArgs& in, int act, hipStream_t s) {
-    return launch_gemm_depth<kGemmDepth>(in, act, s);
+    const int64_t nt = in.I / 128;
+    const int KB = in.K / 128;
+    if (64 * KB <= kGemmPanel && ((int64_t)in.M + 63) / 64 * nt >= 256)
+        return launch_gemm_cfg<2, 2>(in, act, s);
+    return launch_gemm_cfg<1, 2>(in, act, s);
+}
+
+// Weight packing: 16-byte unit i of the packed array is lane (i % 64) of
+// chunk ((i / 64) % 4) of K block ((i / 256) % KB) of 32-row group
+// (i / (256 KB)); it holds the bytes chunk_koff(c, lane / 32) .. +15 of K
+// block kb of row 32 G + lane % 32.
+__global__ __launch_bounds__(256) void k_pack_w(PackArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.units) return;
+    const int lane = (int)(i & 63);
+    const int c = (int)((i >> 6) & 3);
+    const int64_t rest = i >> 8;
+    const int64_t G = rest / a.KB;
+    const int kb = (int)(rest - G * a.KB);
+    const int64_t row = 32 * G + (lane & 31);
+    const uint8_t* src = a.w + row * a.K + kb * 128 + chunk_koff(c, lane >> 5);
+    st128(a.wp + i * 16, ld128(src));
+}
+
+hipError_t launch_pack_w(const PackArgs& in, hipStream_t s) {
+    PackArgs a = in;
+    a.KB = (int)(a.K >> 7);
+    a.units = a.N * a.K / 16;
+    void* args[] = {&a};
+    return hipLaunchKernel((const void*)k_pack_w, dim3((unsigned)((a.units + 255) / 256)),
+                           dim3(256), args, 0, s);
 }
 
 }  // namespace fr

@@ -69,19 +69,29 @@ struct ActArgs {
 struct GemmActArgs {
     const uint8_t* A;       // [M, K] e4m3
     const float* a_scales;  // [M, K/128]
-    const uint8_t* B;       // [2I, K] e4m3, gate/up rows interleaved
+    const uint8_t* B;       // [2I, K] e4m3, gate/up rows interleaved, packed
     const float* b_scales;  // [2I/128, K/128]
     uint8_t* out;           // [M, I]
     float* out_scales;      // [M, I/128]
     int M, K, I;
-    int mt;                 // 32-row tiles
+    int mt;                 // row tiles
     int tiles;              // mt * (I / 128)
     int per_xcd;            // ceil(tiles / 8)
+};
+
+// Weight packing for the GEMM above (a permutation of 16-byte units).
+struct PackArgs {
+    const uint8_t* w;       // [N, K] e4m3 row-major
+    uint8_t* wp;            // packed, N * K bytes
+    int64_t N, K;
+    int KB;                 // K / 128
+    int64_t units;          // N * K / 16
 };
 
 hipError_t launch_norm(const NormArgs& a, int dtype, bool adaptive, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int dtype, hipStream_t s);
 hipError_t launch_act(const ActArgs& a, int dtype, int act, hipStream_t s);
 hipError_t launch_gemm_act(const GemmActArgs& a, int act, hipStream_t s);
+hipError_t launch_pack_w(const PackArgs& a, hipStream_t s);
 
 }  // namespace fr

@@ -28,7 +28,7 @@ def test_header_declares_the_four_ops_and_helpers():
     assert names == sorted([
         "fr_resid_rmsnorm_fp8", "fr_adarms_gate_res_fp8",
         "fr_qkv_normrope_kvwrite", "fr_gated_act_fp8", "fr_gemm_gated_act_fp8",
-        "fr_status_string", "fr_abi_version"])
+        "fr_gemm_pack_weights", "fr_status_string", "fr_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -177,3 +177,18 @@ def test_binding_raises_on_bad_arguments():
 ])
 def test_gemm_gated_act_validation(args, status):
     assert fr.lib.fr_gemm_gated_act_fp8(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, B, 64, 256), fr.FR_ERR_NULL),
+    ((A, None, 64, 256), fr.FR_ERR_NULL),
+    ((A, B, 48, 256), fr.FR_ERR_SHAPE),
+    ((A, B, 64, 200), fr.FR_ERR_SHAPE),
+    ((A, B, -32, 256), fr.FR_ERR_SHAPE),
+    ((A, B, 64, 16384 + 128), fr.FR_ERR_UNSUPPORTED),
+    ((A + 4, B, 64, 256), fr.FR_ERR_ALIGN),
+    ((A, B + 8, 64, 256), fr.FR_ERR_ALIGN),
+    ((A, B, 0, 256), fr.FR_OK),
+])
+def test_gemm_pack_weights_validation(args, status):
+    assert fr.lib.fr_gemm_pack_weights(*args, None) == status

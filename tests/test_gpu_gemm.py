@@ -87,16 +87,46 @@ def check_gemm_interval(q_g, s_g, q_o, s_o, inp, act):
     return ident, float((np.abs(s_g64 - s_o) / s_o).max())
 
 
+def pack_reference(w):
+    """The packed weight layout, written out from its definition in the
+    library header: unit u = ((G * KB + kb) * 4 + c) * 64 + lane holds
+    w[32 G + lane % 32, 128 kb + off : +16] with
+    off = 64 (c // 2) + 32 (lane // 32) + 16 (c % 2)."""
+    N, K = w.shape
+    G, kb, c, lane = np.meshgrid(np.arange(N // 32), np.arange(K // 128),
+                                 np.arange(4), np.arange(64), indexing="ij")
+    row = 32 * G + lane % 32
+    col = 128 * kb + 64 * (c // 2) + 32 * (lane // 32) + 16 * (c % 2)
+    idx = (row * K + col)[..., None] + np.arange(16)
+    return np.ascontiguousarray(w).reshape(-1)[idx.reshape(-1)]
+
+
+def pack_dev(fr, w):
+    N, K = w.shape
+    wp = torch.full((N * K,), 0x7F, dtype=torch.uint8, device="cuda")
+    fr.fr_gemm_pack_weights(to_dev(w), wp, N, K)
+    return wp
+
+
 def run_gemm(fr, inp, act):
     M, K = inp["a"].shape
     I = inp["w"].shape[0] // 2
     q = torch.full((M, I), 0x7F, dtype=torch.uint8, device="cuda")
     sc = torch.full((M, I // 128), float("nan"), dtype=torch.float32, device="cuda")
+    wp = pack_dev(fr, inp["w"])
     fr.fr_gemm_gated_act_fp8(to_dev(inp["a"]), to_dev(inp["a_scales"]),
-                             to_dev(inp["w"]), to_dev(inp["w_scales"]), act, q, sc,
-                             M, K, I)
+                             wp, to_dev(inp["w_scales"]), act, q, sc, M, K, I)
     torch.cuda.synchronize()
     return to_host(q, np.uint8), to_host(sc, np.float32)
+
+
+@pytest.mark.parametrize("N,K", [(32, 128), (64, 384), (12288, 2048)])
+def test_pack_weights_layout(fr, N, K):
+    announce(f"gemm pack weights N={N} K={K}")
+    rng = np.random.default_rng(N + K)
+    w = rng.integers(0, 256, (N, K), dtype=np.uint8)
+    got = to_host(pack_dev(fr, w), np.uint8)
+    assert np.array_equal(got, pack_reference(w))
 
 
 GEMM_CASES = [
@@ -108,6 +138,10 @@ GEMM_CASES = [
     (192, 2048, 6144, oracle.ACT_SWIGLU, 705),           # 2B gate_up, S=192
     (192, 2048, 6144, oracle.ACT_GEGLU_TANH, 705),
     (128, 4096, 12288, oracle.ACT_SWIGLU, 706),          # 8B gate_up, S=128
+    (390, 2048, 6144, oracle.ACT_SWIGLU, 708),           # 64-row tiles, ragged
+    (1000, 2048, 6144, oracle.ACT_SQRELU, 709),          # 128-row tiles, ragged
+    (1024, 4096, 6144, oracle.ACT_SWIGLU, 710),          # 128-row tiles, K = 4096
+    (96, 16384, 256, oracle.ACT_SWIGLU, 711),            # largest K
 ]
 
 
