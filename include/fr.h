@@ -127,14 +127,17 @@ int fr_adarms_gate_res_fp8(const void* x, const void* gate, const void* residual
 
 /*
  * (b) Packed-QKV split + per-head Q/K RMSNorm + RoPE + paged KV write
- *     [FR 二 table step 3, 2.2; FP paged cache]
+ *     [FR 二 table step 3, 2.2; FP paged cache; HY 04 step 10 (the
+ *     attention's Q preparation folded into RoPE)]
  *
  *   qkv row t = [Q heads: Hq*D | K heads: Hkv*D | V heads: Hkv*D], each head
  *     D-contiguous.
  *   For a Q or K head v (D values): if its norm weight is non-NULL,
  *     v = v * rstd(v) * w with rstd over the D values and one weight [D]
  *     shared by all heads; then RoPE at p = positions[t]: pair i
- *     (0 <= i < D/2) turns by p * rope_theta^(-2i/D); then one rounding.
+ *     (0 <= i < D/2) turns by p * rope_theta^(-2i/D); a Q head is then
+ *     multiplied by q_scale (the attention's pre-scale, e.g. 1/sqrt(D);
+ *     1 = none); then one rounding.
  *   q_out[t,h,:] = Q head h;   k_cache[slot,g,:] = K head g;
  *   v_cache[slot,g,:] = V head g copied bit for bit (V is never normed or
  *   rotated).
@@ -151,12 +154,13 @@ int fr_adarms_gate_res_fp8(const void* x, const void* gate, const void* residual
  *   q_out: [T,Hq,D].  k_cache, v_cache: [num_pages, page_size, Hkv, D].
  *   positions and page_table are read on the device, so a captured graph
  *   can be replayed with new positions.
- *   D % 16 == 0, 16 <= D <= 256; Hq, Hkv >= 1; rope_theta > 1 and finite.
+ *   D % 16 == 0, 16 <= D <= 256; Hq, Hkv >= 1; rope_theta > 1 and finite;
+ *   q_scale > 0 and finite.
  */
 int fr_qkv_normrope_kvwrite(const void* qkv, const void* q_norm_w,
                             const void* k_norm_w, float eps,
                             const int32_t* positions, float rope_theta,
-                            int rope_style, void* q_out, void* k_cache,
+                            int rope_style, float q_scale, void* q_out, void* k_cache,
                             void* v_cache, const int32_t* page_table,
                             int32_t page_table_len, int32_t page_size,
                             int32_t num_pages, int32_t* err_flag, int64_t T,

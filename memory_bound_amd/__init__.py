@@ -48,9 +48,9 @@ _SIGS = {
                              _I64, _INT, _P],
     "fr_adarms_gate_res_fp8": [_P, _P, _P, _P, _P, _P, _F, _P, _INT, _F, _P,
                                _I64, _I64, _INT, _P],
-    "fr_qkv_normrope_kvwrite": [_P, _P, _P, _F, _P, _F, _INT, _P, _P, _P, _P,
-                                _I32, _I32, _I32, _P, _I64, _I32, _I32, _I32,
-                                _INT, _P],
+    "fr_qkv_normrope_kvwrite": [_P, _P, _P, _F, _P, _F, _INT, _F, _P, _P, _P,
+                                _P, _I32, _I32, _I32, _P, _I64, _I32, _I32,
+                                _I32, _INT, _P],
     "fr_gated_act_fp8": [_P, _INT, _P, _P, _I64, _I64, _INT, _P],
     "fr_gemm_gated_act_fp8": [_P, _P, _P, _P, _INT, _P, _P, _I64, _I64, _I64,
                               _P],
@@ -143,10 +143,11 @@ def fr_adarms_gate_res_fp8(x, gate, residual, residual_out, ada_scale,
 def fr_qkv_normrope_kvwrite(qkv, q_norm_w, k_norm_w, eps, positions,
                             rope_theta, rope_style, q_out, k_cache, v_cache,
                             page_table, page_table_len, page_size, num_pages,
-                            err_flag, T, Hq, Hkv, D, dtype, stream=None):
+                            err_flag, T, Hq, Hkv, D, dtype, stream=None,
+                            q_scale=1.0):
     _check(lib.fr_qkv_normrope_kvwrite(
         _ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w), eps, _ptr(positions),
-        rope_theta, rope_style, _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
+        rope_theta, rope_style, q_scale, _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
         _ptr(page_table), page_table_len, page_size, num_pages, _ptr(err_flag),
         T, Hq, Hkv, D, dtype, _stream(stream)))
 

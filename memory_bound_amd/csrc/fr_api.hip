@@ -107,7 +107,8 @@ FR_EXPORT int fr_adarms_gate_res_fp8(const void* x, const void* gate,
 FR_EXPORT int fr_qkv_normrope_kvwrite(const void* qkv, const void* q_norm_w,
                                       const void* k_norm_w, float eps,
                                       const int32_t* positions, float rope_theta,
-                                      int rope_style, void* q_out, void* k_cache,
+                                      int rope_style, float q_scale, void* q_out,
+                                      void* k_cache,
                                       void* v_cache, const int32_t* page_table,
                                       int32_t page_table_len, int32_t page_size,
                                       int32_t num_pages, int32_t* err_flag,
@@ -121,6 +122,7 @@ FR_EXPORT int fr_qkv_normrope_kvwrite(const void* qkv, const void* q_norm_w,
     if (rope_style != FR_ROPE_HALF && rope_style != FR_ROPE_INTERLEAVED) return FR_ERR_MODE;
     if (!finite_nonneg(eps)) return FR_ERR_MODE;
     if (!(isfinite(rope_theta) && rope_theta > 1.0f)) return FR_ERR_MODE;
+    if (!(isfinite(q_scale) && q_scale > 0.0f)) return FR_ERR_MODE;
     if (!qkv || !positions || !q_out || !k_cache || !v_cache || !page_table)
         return FR_ERR_NULL;
     if (!aligned16(qkv) || !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -151,6 +153,7 @@ FR_EXPORT int fr_qkv_normrope_kvwrite(const void* qkv, const void* q_norm_w,
     a.style = rope_style;
     a.eps = eps;
     a.theta = rope_theta;
+    a.q_scale = q_scale;
     // one wave per (token, head group); the grid must fit in 32 bits
     if ((T * (int64_t)(Hq + 2 * Hkv)) / 4 + 1 > 0x7fffffffLL) return FR_ERR_UNSUPPORTED;
     return launch_status(fr::launch_qkv(a, dtype, (hipStream_t)stream));

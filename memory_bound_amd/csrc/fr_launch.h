@@ -51,6 +51,7 @@ struct QkvArgs {
     int style;
     float eps;
     float theta;
+    float q_scale;          // multiplies Q after RoPE
 };
 
 // Gated activation on interleaved gate/up + block-128 FP8.

@@ -224,6 +224,11 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
             }
         }
 
+        // attention's Q pre-scale (exact for K: a multiply by 1)
+        const float qs = is_q ? a.q_scale : 1.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] *= qs;
+
         u32x4 o0, o1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

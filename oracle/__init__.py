@@ -89,7 +89,7 @@ def lib():
         L.oracle_adarms_gate_res_fp8.argtypes = [
             _P, _P, _P, _P, _P, _P, _F, _P, _INT, _F, _P, _I64, _I64, _INT]
         L.oracle_qkv_normrope_kvwrite.argtypes = [
-            _P, _P, _P, _F, _P, _F, _INT, _P, _P, _P, _P, _I32, _I32, _I32,
+            _P, _P, _P, _F, _P, _F, _INT, _F, _P, _P, _P, _P, _I32, _I32, _I32,
             _P, _I64, _I32, _I32, _I32, _INT]
         L.oracle_gated_act_fp8.argtypes = [_P, _INT, _P, _P, _I64, _I64, _INT]
         L.oracle_gated_act_fp8_f64.argtypes = [_P, _INT, _P, _P, _I64, _I64]
@@ -262,8 +262,9 @@ def adarms_gate_res_fp8(x, gate, residual, ada_scale, ada_shift, eps, qmode,
 
 def qkv_normrope_kvwrite(qkv, q_norm_w, k_norm_w, eps, positions, rope_theta,
                          rope_style, k_cache, v_cache, page_table, page_size,
-                         Hq, Hkv, D, dtype):
+                         Hq, Hkv, D, dtype, q_scale=1.0):
     """k_cache / v_cache are updated in place (uint16 [pages, P, Hkv, D]).
+    q_scale multiplies Q after RoPE (attention's pre-scale; 1 = none).
     Returns (q_out uint16 [T,Hq,D], err_flag int)."""
     qkv = _c(qkv, np.uint16)
     T = qkv.shape[0]
@@ -278,9 +279,9 @@ def qkv_normrope_kvwrite(qkv, q_norm_w, k_norm_w, eps, positions, rope_theta,
     err = np.zeros(1, dtype=np.int32)
     rc = lib().oracle_qkv_normrope_kvwrite(
         _ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w), eps, _ptr(positions),
-        rope_theta, rope_style, _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
-        _ptr(page_table), page_table.size, page_size, num_pages, _ptr(err), T,
-        Hq, Hkv, D, dtype)
+        rope_theta, rope_style, q_scale, _ptr(q_out), _ptr(k_cache),
+        _ptr(v_cache), _ptr(page_table), page_table.size, page_size, num_pages,
+        _ptr(err), T, Hq, Hkv, D, dtype)
     assert rc == 0
     return q_out, int(err[0])
 

@@ -376,18 +376,20 @@ int oracle_adarms_gate_res_fp8(const uint16_t* x, const uint16_t* gate,
 }
 
 /* Packed QKV split + per-head Q/K RMSNorm + RoPE + KV-cache write [FR
- * section 二 table step 3 and 2.2; FP paged cache]:
+ * section 二 table step 3 and 2.2; FP paged cache; HY 04, step 10: the
+ * attention's Q preparation folded into RoPE]:
  *   row t of qkv = [Q heads (Hq*D) | K heads (Hkv*D) | V heads (Hkv*D)]
  *   Q, K heads: optional RMSNorm over D with a weight shared by all heads
- *   (skipped when the weight pointer is NULL), then RoPE at positions[t],
- *   then one rounding to the storage type.  Q goes to q_out[t, h, :]; K to
+ *   (skipped when the weight pointer is NULL), then RoPE at positions[t];
+ *   Q is then multiplied by q_scale (1 = none); then one rounding to the
+ *   storage type.  Q goes to q_out[t, h, :]; K to
  *   k_cache[slot, g, :]; V is copied bit for bit to v_cache[slot, g, :].
  *   An out-of-range slot skips that token's K/V writes and sets bit 0 of
  *   *err_flag (when err_flag is given). */
 int oracle_qkv_normrope_kvwrite(const uint16_t* qkv, const uint16_t* q_norm_w,
                                 const uint16_t* k_norm_w, float eps,
                                 const int32_t* positions, float rope_theta,
-                                int rope_style, uint16_t* q_out,
+                                int rope_style, float q_scale, uint16_t* q_out,
                                 uint16_t* k_cache, uint16_t* v_cache,
                                 const int32_t* page_table, int32_t page_table_len,
                                 int32_t page_size, int32_t num_pages,
@@ -433,6 +435,8 @@ int oracle_qkv_normrope_kvwrite(const uint16_t* qkv, const uint16_t* q_norm_w,
             or_rope(v, D, pos, (double)rope_theta, rope_style);
             uint16_t* dst;
             if (is_q) {
+                for (int32_t d = 0; d < D; ++d)   /* attention's Q pre-scale */
+                    v[d] *= (double)q_scale;
                 dst = q_out + (t * Hq + h) * D;
             } else {
                 if (slot < 0)

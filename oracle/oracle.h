@@ -82,7 +82,7 @@ int oracle_adarms_gate_res_fp8(const uint16_t* x, const uint16_t* gate,
 int oracle_qkv_normrope_kvwrite(const uint16_t* qkv, const uint16_t* q_norm_w,
                                 const uint16_t* k_norm_w, float eps,
                                 const int32_t* positions, float rope_theta,
-                                int rope_style, uint16_t* q_out,
+                                int rope_style, float q_scale, uint16_t* q_out,
                                 uint16_t* k_cache, uint16_t* v_cache,
                                 const int32_t* page_table, int32_t page_table_len,
                                 int32_t page_size, int32_t num_pages,

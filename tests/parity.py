@@ -139,7 +139,7 @@ def run_adarms(fr, inp, eps, qmode, static_scale, dtype, inplace=False):
 
 
 def run_qkv(fr, inp, eps, theta, style, Hq, Hkv, D, page_size, dtype,
-            err=True):
+            err=True, q_scale=1.0):
     T = inp["qkv"].shape[0]
     kc, vc = to_dev(inp["k_cache"]), to_dev(inp["v_cache"])
     q_out = torch.full((T, Hq, D), POISON16, dtype=torch.int16, device="cuda")
@@ -152,7 +152,7 @@ def run_qkv(fr, inp, eps, theta, style, Hq, Hkv, D, page_size, dtype,
                                style, q_out, kc, vc, table,
                                inp["page_table"].size, page_size,
                                inp["k_cache"].shape[0], ef, T, Hq, Hkv, D,
-                               dtype)
+                               dtype, q_scale=q_scale)
     torch.cuda.synchronize()
     return (to_host(q_out, np.uint16), to_host(kc, np.uint16),
             to_host(vc, np.uint16), int(ef.item()) if err else None)

@@ -108,13 +108,13 @@ def test_adarms_validation():
 
 def qkv(**kw):
     args = dict(qkv=A, q_norm_w=None, k_norm_w=None, eps=1e-6, positions=B,
-                rope_theta=1e4, rope_style=fr.ROPE_HALF, q_out=C, k_cache=D_,
+                rope_theta=1e4, rope_style=fr.ROPE_HALF, q_scale=1.0, q_out=C, k_cache=D_,
                 v_cache=E, page_table=F, page_table_len=1, page_size=1024,
                 num_pages=1, err_flag=None, T=10, Hq=8, Hkv=1, D=256,
                 dtype=fr.F16)
     args.update(kw)
     order = ["qkv", "q_norm_w", "k_norm_w", "eps", "positions", "rope_theta",
-             "rope_style", "q_out", "k_cache", "v_cache", "page_table",
+             "rope_style", "q_scale", "q_out", "k_cache", "v_cache", "page_table",
              "page_table_len", "page_size", "num_pages", "err_flag", "T", "Hq",
              "Hkv", "D", "dtype"]
     return fr.lib.fr_qkv_normrope_kvwrite(*[args[k] for k in order], None)
@@ -133,6 +133,9 @@ def qkv(**kw):
     (dict(rope_style=2), fr.FR_ERR_MODE),
     (dict(rope_theta=1.0), fr.FR_ERR_MODE),
     (dict(rope_theta=float("nan")), fr.FR_ERR_MODE),
+    (dict(q_scale=0.0), fr.FR_ERR_MODE),
+    (dict(q_scale=float("inf")), fr.FR_ERR_MODE),
+    (dict(q_scale=-0.125), fr.FR_ERR_MODE),
     (dict(q_norm_w=G + 8), fr.FR_ERR_ALIGN),
     (dict(positions=B + 2), fr.FR_ERR_ALIGN),
     (dict(err_flag=G + 1), fr.FR_ERR_ALIGN),

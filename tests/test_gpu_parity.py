@@ -179,6 +179,26 @@ def test_qkv_normrope_kvwrite(fr, case):
     check_exact(vc_g, vc_o, "v_cache")
 
 
+@pytest.mark.parametrize("qs", [0.0625, 128 ** -0.5, 3.0])
+def test_qkv_q_prescale(fr, qs):
+    """Q pre-scale folded into RoPE (the attention's Q preparation):
+    Qwen3 prefill shape; a power of two, 1/sqrt(D) and a scale above 1."""
+    T, Hq, Hkv, D, P, pages = 128, 32, 8, 128, 16, 512
+    announce(f"qkv q_scale={qs:.6g} T={T}")
+    inp = workloads.qkv_inputs(T, Hq, Hkv, D, BF16, 408, page_size=P,
+                               num_pages=pages)
+    q_g, kc_g, vc_g, _ = run_qkv(fr, inp, EPS, 1e6, 0, Hq, Hkv, D, P, BF16,
+                                 q_scale=qs)
+    kc_o, vc_o = inp["k_cache"].copy(), inp["v_cache"].copy()
+    q_o, _ = oracle.qkv_normrope_kvwrite(
+        inp["qkv"], inp["q_norm_w"], inp["k_norm_w"], EPS, inp["positions"],
+        1e6, 0, kc_o, vc_o, inp["page_table"], P, Hq, Hkv, D, BF16, q_scale=qs)
+    same = check16(q_g, q_o, BF16, "q_out")
+    announce(f"  q_out bit-identical fraction {same:.6f}")
+    _check_cache(kc_g, kc_o, BF16, "k_cache")
+    check_exact(vc_g, vc_o, "v_cache")
+
+
 def test_qkv_only_q_norm_and_out_of_range(fr):
     T, Hq, Hkv, D, P, pages = 6, 4, 2, 64, 4, 3
     announce("qkv out-of-range positions / q_norm only")

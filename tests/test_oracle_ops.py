@@ -363,6 +363,42 @@ def test_qkv_op_without_norm_and_out_of_range_positions():
     assert written.sum() == 2
 
 
+def test_qkv_op_q_prescale():
+    """Q pre-scale folded into RoPE ([HY] 04 step 10): Q only, K/V untouched;
+    a power-of-two scale commutes with rounding (exact); any scale gives the
+    correctly rounded s * y of the pinned composition."""
+    dt = oracle.BF16
+    T, Hq, Hkv, D, P, pages = 6, 4, 2, 64, 4, 4
+    inp = workloads.qkv_inputs(T, Hq, Hkv, D, dt, seed=24, page_size=P,
+                               num_pages=pages)
+    outs = {}
+    for qs in (1.0, 0.25, 64 ** -0.5):
+        kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
+        q_out, _ = oracle.qkv_normrope_kvwrite(
+            inp["qkv"], inp["q_norm_w"], inp["k_norm_w"], EPS,
+            inp["positions"], 1e6, oracle.ROPE_HALF, kc, vc,
+            inp["page_table"], P, Hq, Hkv, D, dt, q_scale=qs)
+        outs[qs] = (q_out, kc, vc)
+    base = outs[1.0]
+    for qs in (0.25, 64 ** -0.5):
+        assert np.array_equal(outs[qs][1], base[1])
+        assert np.array_equal(outs[qs][2], base[2])
+    # power of two: exactly a quarter of the unscaled values (no subnormals here)
+    assert np.array_equal(_dec(outs[0.25][0], dt), 0.25 * _dec(base[0], dt))
+    # general scale: the correctly rounded product of the float64 composition
+    qkv = _dec(inp["qkv"], dt).reshape(T, Hq + 2 * Hkv, D)
+    qw = _dec(inp["q_norm_w"], dt)
+    s = 64 ** -0.5
+    got = _dec(outs[s][0], dt)
+    for t in range(T):
+        for h in range(Hq):
+            y = s * oracle.rope(oracle.rmsnorm(qkv[t, h], qw, oracle.W_MUL, EPS),
+                                int(inp["positions"][t]), 1e6)
+            mag = outs[s][0][t, h] & 0x7FFF               # spacing above |got|
+            ulp = _dec(mag + 1, dt) - _dec(mag, dt)
+            assert np.all(np.abs(got[t, h] - y) <= 0.5 * ulp)
+
+
 @pytest.mark.parametrize("kind", [oracle.ACT_SWIGLU, oracle.ACT_GEGLU_TANH,
                                   oracle.ACT_SQRELU])
 def test_gated_act_block_worked_example(kind):
