@@ -84,6 +84,19 @@ def lib():
         L.or_quant_dynamic.restype = _F
         L.or_kv_slot.argtypes = [_I64, _P, _I32, _I32, _I32]
         L.or_kv_slot.restype = _I64
+        L.or_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.or_e2m1_decode.restype = _D
+        L.or_e2m1_encode.argtypes = [_D]
+        L.or_e2m1_encode.restype = ctypes.c_uint8
+        L.or_mx_scale_code.argtypes = [_D]
+        L.or_mx_scale_code.restype = _INT
+        L.or_quant_mxfp4.argtypes = [_P, _I64, _P, _P]
+        L.or_quant_mxfp4.restype = None
+        L.oracle_resid_rmsnorm_mxfp4.argtypes = [
+            _P, _P, _P, _P, _INT, _F, _P, _P, _I64, _I64, _INT]
+        L.oracle_resid_rmsnorm_mxfp4.restype = _INT
+        L.oracle_gated_act_mxfp4.argtypes = [_P, _INT, _P, _P, _I64, _I64, _INT]
+        L.oracle_gated_act_mxfp4.restype = _INT
         L.oracle_resid_rmsnorm_fp8.argtypes = [
             _P, _P, _P, _P, _INT, _F, _P, _INT, _F, _P, _I64, _I64, _INT]
         L.oracle_adarms_gate_res_fp8.argtypes = [
@@ -168,6 +181,37 @@ def encode16_n(v, dtype):
 
 def e4m3_table():
     return np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def e2m1_decode(c):
+    return lib().or_e2m1_decode(int(c))
+
+
+def e2m1_encode(v):
+    return lib().or_e2m1_encode(float(v))
+
+
+def mx_scale_code(amax):
+    return lib().or_mx_scale_code(float(amax))
+
+
+def quant_mxfp4(y):
+    """y: float64 [n], n % 32 == 0 -> (packed uint8 [n/2], scales uint8 [n/32])."""
+    y = _c(np.ravel(y), np.float64)
+    assert y.size % 32 == 0
+    packed = np.empty(y.size // 2, dtype=np.uint8)
+    scales = np.empty(y.size // 32, dtype=np.uint8)
+    lib().or_quant_mxfp4(_ptr(y), y.size, _ptr(packed), _ptr(scales))
+    return packed, scales
+
+
+def unpack_fp4(packed):
+    """uint8 [..., n/2] -> 4-bit codes uint8 [..., n] (low nibble first)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
 
 
 # ---- building blocks --------------------------------------------------------
@@ -295,6 +339,36 @@ def gated_act_fp8(gate_up, act_kind, dtype):
     sc = np.empty((T, I // 128), dtype=np.float32)
     rc = lib().oracle_gated_act_fp8(_ptr(gate_up), act_kind, _ptr(q), _ptr(sc),
                                     T, I, dtype)
+    assert rc == 0
+    return q, sc
+
+
+def resid_rmsnorm_mxfp4(x, residual, weight, wmode, eps, dtype):
+    """Returns (residual_out uint16 [T,H], out_fp4 uint8 [T,H/2],
+    out_scales uint8 [T,H/32] E8M0 codes)."""
+    x = _c(x, np.uint16)
+    residual = _c(residual, np.uint16)
+    T, H = x.shape
+    weight = _c(weight, np.uint16)
+    ro = np.empty_like(x)
+    q = np.empty((T, H // 2), dtype=np.uint8)
+    sc = np.empty((T, H // 32), dtype=np.uint8)
+    rc = lib().oracle_resid_rmsnorm_mxfp4(
+        _ptr(x), _ptr(residual), _ptr(ro), _ptr(weight), wmode, eps, _ptr(q),
+        _ptr(sc), T, H, dtype)
+    assert rc == 0
+    return ro, q, sc
+
+
+def gated_act_mxfp4(gate_up, act_kind, dtype):
+    """Returns (out_fp4 uint8 [T,I/2], out_scales uint8 [T,I/32])."""
+    gate_up = _c(gate_up, np.uint16)
+    T, I2 = gate_up.shape
+    I = I2 // 2
+    q = np.empty((T, I // 2), dtype=np.uint8)
+    sc = np.empty((T, I // 32), dtype=np.uint8)
+    rc = lib().oracle_gated_act_mxfp4(_ptr(gate_up), act_kind, _ptr(q),
+                                      _ptr(sc), T, I, dtype)
     assert rc == 0
     return q, sc
 

@@ -275,6 +275,71 @@ float or_quant_dynamic(const double* y, int64_t n, uint8_t* q)
     return s;
 }
 
+/* ---- MX FP4 [HY 04 steps 5 and 9, 06 census: the residual-RMSNorm and
+ * SwiGLU producers that feed FP4 GEMMs].  The pages name the producers but
+ * not the format; the reading taken is the OCP Microscaling format MXFP4:
+ * E2M1 elements (sign, 2 exponent bits with bias 1, 1 mantissa bit; the
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) in blocks of 32 sharing one
+ * power-of-two scale stored as E8M0 (2^(code - 127)). ---- */
+
+double or_e2m1_decode(uint8_t code)
+{
+    int s = (code >> 3) & 1, E = (code >> 1) & 3, M = code & 1;
+    double a = (E == 0) ? 0.5 * M : ldexp(1.0 + 0.5 * M, E - 1);
+    return s ? -a : a;
+}
+
+/* Round to nearest on the E2M1 grid, ties to the even code (the even
+ * mantissa), magnitudes at or above 6 saturate to 6; the sign bit is the
+ * input's sign, also when the value rounds to zero. */
+uint8_t or_e2m1_encode(double v)
+{
+    uint8_t s = signbit(v) ? 8 : 0;
+    double a = fabs(v);
+    if (!(a < 6.0))                             /* also inf and NaN */
+        return s | 7;
+    double r = round_to_format(a, 2, 0);        /* 2 significant bits, emin 0 */
+    return s | (uint8_t)pack_bits(r, 2, 1, 0, 2);
+}
+
+/* The block scale is 2^(floor(log2 amax) - 2): 2 is the exponent of the
+ * largest E2M1 value, so the block maximum lands in [4, 8) before
+ * rounding.  Clamped to the E8M0 range [2^-127, 2^127]; an all-zero
+ * block gets the smallest scale. */
+int or_mx_scale_code(double amax)
+{
+    if (!(amax > 0.0))
+        return 0;
+    int e;
+    frexp(amax, &e);                            /* amax = f 2^e, f in [0.5, 1) */
+    int x = (e - 1) - 2;
+    if (x < -127) x = -127;
+    if (x > 127) x = 127;
+    return x + 127;
+}
+
+/* Blocks of 32 consecutive values: scales[b] = E8M0 code, and element i
+ * of the block is E2M1(y_i / 2^(code - 127)); two elements per byte,
+ * element 2k in bits 3..0 and 2k+1 in bits 7..4. */
+void or_quant_mxfp4(const double* y, int64_t n, uint8_t* packed, uint8_t* scales)
+{
+    for (int64_t b = 0; b < n / 32; ++b) {
+        const double* yb = y + b * 32;
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i)
+            if (fabs(yb[i]) > amax)
+                amax = fabs(yb[i]);
+        int code = or_mx_scale_code(amax);
+        scales[b] = (uint8_t)code;
+        double X = ldexp(1.0, code - 127);
+        for (int i = 0; i < 32; i += 2) {
+            uint8_t lo = or_e2m1_encode(yb[i] / X);
+            uint8_t hi = or_e2m1_encode(yb[i + 1] / X);
+            packed[(b * 32 + i) / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
 /* Paged KV-cache slot of a token position [FP, paged cache]: page
  * page_table[pos / page_size], offset pos % page_size.  -1 when the
  * position, the table entry or the page is out of range. */
@@ -330,6 +395,41 @@ int oracle_resid_rmsnorm_fp8(const uint16_t* x, const uint16_t* residual,
             or_quant_static(y, H, (double)static_scale, out_fp8 + t * H);
         else
             out_scales[t] = or_quant_dynamic(y, H, out_fp8 + t * H);
+    }
+    free(ro); free(w); free(y);
+    return 0;
+}
+
+/* Residual add + RMSNorm + MX FP4 [HY 04 step 5, 06 census: the residual
+ * RMSNorm FP4 producer]: residual_out and y as in the op above; y is
+ * quantised to MXFP4 in blocks of 32 along the row (out_fp4 [T, H/2],
+ * out_scales [T, H/32] E8M0 codes). */
+int oracle_resid_rmsnorm_mxfp4(const uint16_t* x, const uint16_t* residual,
+                               uint16_t* residual_out, const uint16_t* weight,
+                               int wmode, float eps, uint8_t* out_fp4,
+                               uint8_t* out_scales, int64_t T, int64_t H,
+                               int dtype)
+{
+    if (H % 32 != 0)
+        return -2;
+    double* ro = malloc(sizeof(double) * (size_t)H);
+    double* w = malloc(sizeof(double) * (size_t)H);
+    double* y = malloc(sizeof(double) * (size_t)H);
+    if (!ro || !w || !y) {
+        free(ro); free(w); free(y);
+        return -1;
+    }
+    for (int64_t j = 0; j < H; ++j)
+        w[j] = (wmode != OR_W_NONE) ? dec16(weight[j], dtype) : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t j = 0; j < H; ++j) {
+            uint16_t b = enc16(dec16(x[t * H + j], dtype) + dec16(residual[t * H + j], dtype),
+                               dtype);
+            residual_out[t * H + j] = b;
+            ro[j] = dec16(b, dtype);
+        }
+        or_rmsnorm(ro, w, wmode, H, (double)eps, y);
+        or_quant_mxfp4(y, H, out_fp4 + t * (H / 2), out_scales + t * (H / 32));
     }
     free(ro); free(w); free(y);
     return 0;
@@ -475,6 +575,27 @@ int oracle_gated_act_fp8_f64(const double* gate_up, int act, uint8_t* out_fp8,
                 or_quant_dynamic(h, B, out_fp8 + t * I + b * B);
         }
     }
+    return 0;
+}
+
+/* Gated activation + MX FP4 [HY 04 step 9, 06 census: the SwiGLU FP4
+ * producer]: h = act(g) * u in double, quantised to MXFP4 in blocks of 32
+ * outputs (out_fp4 [T, I/2], out_scales [T, I/32] E8M0 codes). */
+int oracle_gated_act_mxfp4(const uint16_t* gate_up, int act, uint8_t* out_fp4,
+                           uint8_t* out_scales, int64_t T, int64_t I, int dtype)
+{
+    if (I % 32 != 0)
+        return -2;
+    double* h = malloc(sizeof(double) * (size_t)I);
+    if (!h)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* gu = gate_up + t * 2 * I;
+        for (int64_t j = 0; j < I; ++j)
+            h[j] = or_act(dec16(gu[2 * j], dtype), act) * dec16(gu[2 * j + 1], dtype);
+        or_quant_mxfp4(h, I, out_fp4 + t * (I / 2), out_scales + t * (I / 32));
+    }
+    free(h);
     return 0;
 }
 

@@ -62,6 +62,11 @@ void   or_rope(double* v, int64_t D, int64_t pos, double theta, int style);
 double or_act(double g, int act);
 void   or_quant_static(const double* y, int64_t n, double mult, uint8_t* q);
 float  or_quant_dynamic(const double* y, int64_t n, uint8_t* q);
+double  or_e2m1_decode(uint8_t code);        /* 4-bit code, sign in bit 3 */
+uint8_t or_e2m1_encode(double v);            /* RNE, |v| >= 6 -> 6, sign kept */
+int     or_mx_scale_code(double amax);       /* E8M0 code of the MX block scale */
+void    or_quant_mxfp4(const double* y, int64_t n, uint8_t* packed,
+                       uint8_t* scales);     /* n % 32 == 0 */
 int64_t or_kv_slot(int64_t pos, const int32_t* page_table, int32_t table_len,
                    int32_t page_size, int32_t num_pages);
 
@@ -91,6 +96,13 @@ int oracle_qkv_normrope_kvwrite(const uint16_t* qkv, const uint16_t* q_norm_w,
 
 int oracle_gated_act_fp8(const uint16_t* gate_up, int act, uint8_t* out_fp8,
                          float* out_scales, int64_t T, int64_t I, int dtype);
+int oracle_resid_rmsnorm_mxfp4(const uint16_t* x, const uint16_t* residual,
+                               uint16_t* residual_out, const uint16_t* weight,
+                               int wmode, float eps, uint8_t* out_fp4,
+                               uint8_t* out_scales, int64_t T, int64_t H,
+                               int dtype);
+int oracle_gated_act_mxfp4(const uint16_t* gate_up, int act, uint8_t* out_fp4,
+                           uint8_t* out_scales, int64_t T, int64_t I, int dtype);
 int oracle_gated_act_fp8_f64(const double* gate_up, int act, uint8_t* out_fp8,
                              float* out_scales, int64_t T, int64_t I);
 
