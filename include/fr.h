@@ -188,6 +188,40 @@ int fr_gated_act_fp8(const void* gate_up, int act, uint8_t* out_fp8,
                      void* stream);
 
 /*
+ * MX FP4 producers [HY 04 steps 5 and 9, 06 census: the residual-RMSNorm
+ *     and SwiGLU FP4 producers that feed FP4 GEMMs].  Format (OCP
+ *     Microscaling MXFP4): blocks of 32 consecutive values of a row share
+ *     one E8M0 scale code c (scale 2^(c - 127)); each value is an E2M1 code
+ *     (sign in bit 3; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte,
+ *     the even-indexed value in bits 3..0.
+ *   c = clamp(floor(log2 amax) - 2 + 127, 0, 254) with amax the block's
+ *     largest magnitude (c = 0 for an all-zero block); element =
+ *     E2M1(v / 2^(c - 127)) rounded to nearest even, magnitudes >= 6
+ *     saturate to 6, the sign kept also when the value rounds to zero.
+ *
+ * (a-fp4) residual add + RMSNorm + MXFP4: residual_out and the normalised
+ *   value y exactly as fr_resid_rmsnorm_fp8 (wmode FR_W_NONE / MUL /
+ *   ONE_PLUS); y is quantised in blocks of 32 along H.  The codes and scales
+ *   are those of the exact y (the kernel takes every rounding decision on
+ *   the exact value).  out_fp4: [T, H/2] bytes (16-byte aligned);
+ *   out_scales: [T, H/32] bytes.  H % 32 == 0, H <= 32768.  x, residual,
+ *   residual_out (may equal residual), weight: as fr_resid_rmsnorm_fp8.
+ */
+int fr_resid_rmsnorm_mxfp4(const void* x, const void* residual,
+                           void* residual_out, const void* weight, int wmode,
+                           float eps, uint8_t* out_fp4, uint8_t* out_scales,
+                           int64_t T, int64_t H, int dtype, void* stream);
+
+/*
+ * (c-fp4) gated activation + MXFP4: h = act(g) * u as fr_gated_act_fp8 (fp32
+ *   activation), quantised in blocks of 32 outputs.  out_fp4: [T, I/2]
+ *   bytes (16-byte aligned); out_scales: [T, I/32] bytes.  I % 128 == 0.
+ */
+int fr_gated_act_mxfp4(const void* gate_up, int act, uint8_t* out_fp4,
+                       uint8_t* out_scales, int64_t T, int64_t I, int dtype,
+                       void* stream);
+
+/*
  * (c') FP8 gate_up GEMM fused with the gated activation and block-128 FP8
  *      [SM89 Phase 2 (gate_up GEMM + silu*up + per-token block-128 FP8 in
  *      one launch, no [S, 2*inter] bf16 intermediate); FP third technique

@@ -55,6 +55,9 @@ _SIGS = {
     "fr_gemm_gated_act_fp8": [_P, _P, _P, _P, _INT, _P, _P, _I64, _I64, _I64,
                               _P],
     "fr_gemm_pack_weights": [_P, _P, _I64, _I64, _P],
+    "fr_resid_rmsnorm_mxfp4": [_P, _P, _P, _P, _INT, _F, _P, _P, _I64, _I64,
+                               _INT, _P],
+    "fr_gated_act_mxfp4": [_P, _INT, _P, _P, _I64, _I64, _INT, _P],
 }
 
 
@@ -156,6 +159,20 @@ def fr_gated_act_fp8(gate_up, act, out_fp8, out_scales, T, I, dtype,
                      stream=None):
     _check(lib.fr_gated_act_fp8(
         _ptr(gate_up), act, _ptr(out_fp8), _ptr(out_scales), T, I, dtype,
+        _stream(stream)))
+
+
+def fr_resid_rmsnorm_mxfp4(x, residual, residual_out, weight, wmode, eps,
+                           out_fp4, out_scales, T, H, dtype, stream=None):
+    _check(lib.fr_resid_rmsnorm_mxfp4(
+        _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(weight), wmode, eps,
+        _ptr(out_fp4), _ptr(out_scales), T, H, dtype, _stream(stream)))
+
+
+def fr_gated_act_mxfp4(gate_up, act, out_fp4, out_scales, T, I, dtype,
+                       stream=None):
+    _check(lib.fr_gated_act_mxfp4(
+        _ptr(gate_up), act, _ptr(out_fp4), _ptr(out_scales), T, I, dtype,
         _stream(stream)))
 
 

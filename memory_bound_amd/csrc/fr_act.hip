@@ -21,6 +21,12 @@
 // clamp.  (Measured on MI355X at 8192 x 12288: this layout with 4 waves per
 // workgroup is 5-15% faster than 2 or 8 waves per workgroup or 32-byte
 // lane-contiguous chunks.)
+//
+// MX FP4 output (Hy-Embodied report, 04 step 9 and 06: the SwiGLU FP4
+// producer): the same loads and activation; a block of 32 outputs is 8
+// consecutive lanes, its maximum a DPP reduction over 8 lanes, whose fp32
+// exponent gives the E8M0 code; the 4 outputs of a lane become 16 bits of
+// E2M1 codes after an exact power-of-two scaling.
 #include "fr_device.h"
 #include "fr_launch.h"
 
@@ -28,8 +34,10 @@ namespace fr {
 
 constexpr int kActSteps = 8;   // block pairs per wave (bandwidth regime)
 
-// STEPS: block pairs per wave; NTL / NTS: non-temporal loads / stores.
-template <int DT, int ACT, int STEPS = kActSteps, bool NTL = true, bool NTS = true>
+// STEPS: block pairs per wave; NTL / NTS: non-temporal loads / stores;
+// MX: MX FP4 output instead of block-128 FP8.
+template <int DT, int ACT, int STEPS = kActSteps, bool NTL = true, bool NTS = true,
+          bool MX = false>
 __global__ __launch_bounds__(256) void k_act(ActArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -63,6 +71,21 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
             h[e] = gate_act<ACT>(lo16<DT>(in[k][e])) * hi16<DT>(in[k][e]);
             m = fmaxf(m, fabsf(h[e]));
         }
+        if constexpr (MX) {
+            m = group_reduce<8>(m, OpMax());             // block of 32 outputs
+            const int code = mx_code(m);
+            const u32 p = pack_e2m1x4(h[0], h[1], h[2], h[3], mx_mult(code));
+            const int b = blk[k];
+            if (b < a.nb) {
+                uint16_t* dst = (uint16_t*)(a.out + t * (int64_t)(a.I >> 1) +
+                                            (unsigned)b * 64u + (unsigned)cb * 2u);
+                if constexpr (NTS) __builtin_nontemporal_store((uint16_t)p, dst);
+                else *dst = (uint16_t)p;
+                if ((cb & 7) == 0)
+                    a.mx_scales[t * (int64_t)(a.I >> 5) + b * 4 + (cb >> 3)] = (uint8_t)code;
+            }
+            continue;
+        }
         // Block maximum over 32 lanes (all 64 lanes take part).
         m = group_reduce<16>(m, OpMax());
         m = rows_pair(m, OpMax());
@@ -81,6 +104,7 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
         const float s_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(si, 32));
         sc = lane == 2 * k ? s_lo : (lane == 2 * k + 1 ? s_hi : sc);
     }
+    if constexpr (MX) return;
     // one contiguous store of the wave's 2 * STEPS block scales
     const int b0 = wc * STEPS * 2;
     if (lane < 2 * STEPS && b0 + lane < a.nb) {
@@ -88,7 +112,7 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
     }
 }
 
-template <int DT, int STEPS, bool NTL, bool NTS>
+template <int DT, int STEPS, bool NTL, bool NTS, bool MX>
 static hipError_t launch_act_cfg(const ActArgs& in, int act, hipStream_t s) {
     ActArgs a = in;
     const int per_wave = 2 * STEPS;                      // blocks per wave
@@ -96,9 +120,9 @@ static hipError_t launch_act_cfg(const ActArgs& in, int act, hipStream_t s) {
     a.waves = a.T * a.wpr;
     const void* fn;
     switch (act) {
-    case ACT_SWIGLU: fn = (const void*)k_act<DT, ACT_SWIGLU, STEPS, NTL, NTS>; break;
-    case ACT_GEGLU_TANH: fn = (const void*)k_act<DT, ACT_GEGLU_TANH, STEPS, NTL, NTS>; break;
-    default: fn = (const void*)k_act<DT, ACT_SQRELU, STEPS, NTL, NTS>; break;
+    case ACT_SWIGLU: fn = (const void*)k_act<DT, ACT_SWIGLU, STEPS, NTL, NTS, MX>; break;
+    case ACT_GEGLU_TANH: fn = (const void*)k_act<DT, ACT_GEGLU_TANH, STEPS, NTL, NTS, MX>; break;
+    default: fn = (const void*)k_act<DT, ACT_SQRELU, STEPS, NTL, NTS, MX>; break;
     }
     void* args[] = {&a};
     const unsigned blocks = (unsigned)((a.waves + 3) / 4);
@@ -110,15 +134,20 @@ static hipError_t launch_act_cfg(const ActArgs& in, int act, hipStream_t s) {
 // (~6.1 TB/s): 4 pairs with non-temporal stores ~3-6% slower, cacheable loads
 // ~15% slower.  Small batches: 2 block pairs per wave for more parallel waves,
 // everything cacheable for the next op.
-hipError_t launch_act(const ActArgs& in, int dtype, int act, hipStream_t s) {
-    ActArgs a = in;
-    a.nb = a.I / 128;
+template <bool MX>
+static hipError_t launch_act_fmt(const ActArgs& a, int dtype, int act, hipStream_t s) {
     const bool big = a.T >= 2048;
     if (dtype == DT_BF16)
-        return big ? launch_act_cfg<DT_BF16, kActSteps, true, false>(a, act, s)
-                   : launch_act_cfg<DT_BF16, 2, false, false>(a, act, s);
-    return big ? launch_act_cfg<DT_F16, kActSteps, true, false>(a, act, s)
-               : launch_act_cfg<DT_F16, 2, false, false>(a, act, s);
+        return big ? launch_act_cfg<DT_BF16, kActSteps, true, false, MX>(a, act, s)
+                   : launch_act_cfg<DT_BF16, 2, false, false, MX>(a, act, s);
+    return big ? launch_act_cfg<DT_F16, kActSteps, true, false, MX>(a, act, s)
+               : launch_act_cfg<DT_F16, 2, false, false, MX>(a, act, s);
+}
+
+hipError_t launch_act(const ActArgs& in, int dtype, int act, bool mx, hipStream_t s) {
+    ActArgs a = in;
+    a.nb = a.I / 128;
+    return mx ? launch_act_fmt<true>(a, dtype, act, s) : launch_act_fmt<false>(a, dtype, act, s);
 }
 
 }  // namespace fr

@@ -68,7 +68,7 @@ FR_EXPORT int fr_resid_rmsnorm_fp8(const void* x, const void* residual,
     a.qmode = qmode;
     a.eps = eps;
     a.static_scale = static_scale;
-    return launch_status(fr::launch_norm(a, dtype, false, (hipStream_t)stream));
+    return launch_status(fr::launch_norm(a, dtype, fr::NORM_FP8, (hipStream_t)stream));
 }
 
 FR_EXPORT int fr_adarms_gate_res_fp8(const void* x, const void* gate,
@@ -101,7 +101,7 @@ FR_EXPORT int fr_adarms_gate_res_fp8(const void* x, const void* gate,
     a.qmode = qmode;
     a.eps = eps;
     a.static_scale = static_scale;
-    return launch_status(fr::launch_norm(a, dtype, true, (hipStream_t)stream));
+    return launch_status(fr::launch_norm(a, dtype, fr::NORM_ADA_FP8, (hipStream_t)stream));
 }
 
 FR_EXPORT int fr_qkv_normrope_kvwrite(const void* qkv, const void* q_norm_w,
@@ -180,7 +180,63 @@ FR_EXPORT int fr_gated_act_fp8(const void* gate_up, int act, uint8_t* out_fp8,
     a.scales = out_scales;
     a.T = T;
     a.I = (int)I;
-    return launch_status(fr::launch_act(a, dtype, act, (hipStream_t)stream));
+    return launch_status(fr::launch_act(a, dtype, act, false, (hipStream_t)stream));
+}
+
+FR_EXPORT int fr_resid_rmsnorm_mxfp4(const void* x, const void* residual,
+                                     void* residual_out, const void* weight,
+                                     int wmode, float eps, uint8_t* out_fp4,
+                                     uint8_t* out_scales, int64_t T, int64_t H,
+                                     int dtype, void* stream) {
+    if (dtype != FR_F16 && dtype != FR_BF16) return FR_ERR_DTYPE;
+    if (T < 0 || H <= 0 || H % 32 != 0) return FR_ERR_SHAPE;
+    if (H > 32768) return FR_ERR_UNSUPPORTED;
+    if (T > 0x7fffffffLL) return FR_ERR_UNSUPPORTED;          // grid limit
+    if (wmode != FR_W_NONE && wmode != FR_W_MUL && wmode != FR_W_ONE_PLUS) return FR_ERR_MODE;
+    if (!finite_nonneg(eps)) return FR_ERR_MODE;
+    if (!x || !residual || !residual_out || !out_fp4 || !out_scales) return FR_ERR_NULL;
+    if (wmode != FR_W_NONE && !weight) return FR_ERR_NULL;
+    if (!aligned16(x) || !aligned16(residual) || !aligned16(residual_out) ||
+        !aligned16(out_fp4))
+        return FR_ERR_ALIGN;
+    if (wmode != FR_W_NONE && !aligned16(weight)) return FR_ERR_ALIGN;
+    if (T == 0) return FR_OK;
+
+    fr::NormArgs a{};
+    a.x = x;
+    a.res = residual;
+    a.res_out = residual_out;
+    a.w = weight;
+    a.out = out_fp4;
+    a.mx_scales = out_scales;
+    a.T = T;
+    a.H = (int)H;
+    a.wmode = wmode;
+    a.eps = eps;
+    a.static_scale = 1.0f;
+    return launch_status(fr::launch_norm(a, dtype, fr::NORM_MXFP4, (hipStream_t)stream));
+}
+
+FR_EXPORT int fr_gated_act_mxfp4(const void* gate_up, int act, uint8_t* out_fp4,
+                                 uint8_t* out_scales, int64_t T, int64_t I,
+                                 int dtype, void* stream) {
+    if (dtype != FR_F16 && dtype != FR_BF16) return FR_ERR_DTYPE;
+    if (T < 0 || I <= 0 || I % 128 != 0) return FR_ERR_SHAPE;
+    if (I > (1 << 24)) return FR_ERR_UNSUPPORTED;
+    if (act != FR_ACT_SWIGLU && act != FR_ACT_GEGLU_TANH && act != FR_ACT_SQRELU)
+        return FR_ERR_MODE;
+    if (!gate_up || !out_fp4 || !out_scales) return FR_ERR_NULL;
+    if (!aligned16(gate_up) || !aligned16(out_fp4)) return FR_ERR_ALIGN;
+    if (T == 0) return FR_OK;
+    if (T * ((I + 1023) / 1024) / 4 + 1 > 0x7fffffffLL) return FR_ERR_UNSUPPORTED;
+
+    fr::ActArgs a{};
+    a.gu = gate_up;
+    a.out = out_fp4;
+    a.mx_scales = out_scales;
+    a.T = T;
+    a.I = (int)I;
+    return launch_status(fr::launch_act(a, dtype, act, true, (hipStream_t)stream));
 }
 
 FR_EXPORT int fr_gemm_gated_act_fp8(const uint8_t* a, const float* a_scales,

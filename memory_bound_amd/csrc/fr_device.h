@@ -221,6 +221,38 @@ __device__ __forceinline__ float div448(float amax) {
 // ---------------------------------------------------------------------------
 // Global memory access: 128-bit vector loads/stores.
 // ---------------------------------------------------------------------------
+// MX FP4 (OCP MXFP4: E2M1 elements, blocks of 32, E8M0 scale).  The block
+// scale is 2^(floor(log2 amax) - 2), so the block maximum lands in [4, 8):
+// with E the biased fp32 exponent of amax, the E8M0 code is E - 2 (0 for
+// amax below 2^-124, zero included), and the elements are amax-relative
+// values times 2^(127 - code), a power of two (exact).  The conversion
+// v_cvt_scalef32_pk_fp4_f32 rounds to nearest even on the E2M1 grid,
+// saturates at 6 and keeps the sign of values that round to zero (checked
+// on MI355X); with scale 1 it converts the values as given.
+__device__ __forceinline__ int mx_code(float amax) {
+    const int E = (int)((__builtin_bit_cast(u32, amax) >> 23) & 0xFF);
+    return E > 2 ? E - 2 : 0;
+}
+__device__ __forceinline__ float mx_mult(int code) {          // 2^(127 - code)
+    return __builtin_bit_cast(float, (u32)(254 - code) << 23);
+}
+// 8 values -> 8 E2M1 codes, value 2i in the low nibble of byte i.
+__device__ __forceinline__ u32 pack_e2m1x8(const float* v, float m) {
+    u32 p = 0;
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0] * m, v[1] * m, 1.0f, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2] * m, v[3] * m, 1.0f, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4] * m, v[5] * m, 1.0f, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6] * m, v[7] * m, 1.0f, 3);
+    return p;
+}
+// 4 values -> 4 E2M1 codes in the low 16 bits.
+__device__ __forceinline__ u32 pack_e2m1x4(float a, float b, float c, float d, float m) {
+    u32 p = 0;
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, a * m, b * m, 1.0f, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, c * m, d * m, 1.0f, 1);
+    return p;
+}
+
 __device__ __forceinline__ u32x4 ld128(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }

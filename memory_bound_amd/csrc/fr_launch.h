@@ -18,8 +18,9 @@ struct NormArgs {
     const void* w;          // [H]     (plain variant, FR_W_MUL / FR_W_ONE_PLUS)
     const void* ada_scale;  // [T,H]   (adaptive variant only)
     const void* ada_shift;  // [T,H]   (adaptive variant only)
-    uint8_t* out;           // [T,H]
+    uint8_t* out;           // [T,H] FP8, or [T,H/2] MX FP4
     float* scales;          // [T]     (FR_Q_TOKEN)
+    uint8_t* mx_scales;     // [T,H/32] E8M0 (MX FP4 output)
     int64_t T;
     int H;
     int nw;                 // wavefronts per row
@@ -57,8 +58,9 @@ struct QkvArgs {
 // Gated activation on interleaved gate/up + block-128 FP8.
 struct ActArgs {
     const void* gu;         // [T,2I]
-    uint8_t* out;           // [T,I]
+    uint8_t* out;           // [T,I] FP8, or [T,I/2] MX FP4
     float* scales;          // [T,I/128]
+    uint8_t* mx_scales;     // [T,I/32] E8M0 (MX FP4 output)
     int64_t T;
     int64_t waves;          // T * wpr
     int I;
@@ -89,9 +91,10 @@ struct PackArgs {
     int64_t units;          // N * K / 16
 };
 
-hipError_t launch_norm(const NormArgs& a, int dtype, bool adaptive, hipStream_t s);
+enum { NORM_FP8 = 0, NORM_ADA_FP8 = 1, NORM_MXFP4 = 2 };
+hipError_t launch_norm(const NormArgs& a, int dtype, int kind, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int dtype, hipStream_t s);
-hipError_t launch_act(const ActArgs& a, int dtype, int act, hipStream_t s);
+hipError_t launch_act(const ActArgs& a, int dtype, int act, bool mx, hipStream_t s);
 hipError_t launch_gemm_act(const GemmActArgs& a, int act, hipStream_t s);
 hipError_t launch_pack_w(const PackArgs& a, hipStream_t s);
 

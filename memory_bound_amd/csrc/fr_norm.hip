@@ -28,6 +28,15 @@
 // follows is the rounding of the exact value to within ~2^-46.  Without this,
 // rows where rstd cancels against the per-token scale (no weight) put many
 // values exactly on e4m3 rounding midpoints and fp32 noise picks the side.
+//
+// MX FP4 output (plain modes; Hy-Embodied report, 04 step 5 and 06: the
+// residual RMSNorm FP4 producer): the same rounded-to-odd products y_j, in
+// blocks of 32 values = 4 consecutive lanes; the block maximum is a DPP
+// quad reduction, its fp32 exponent gives the E8M0 code, and the elements
+// are converted by the hardware E2M1 conversion after an exact power-of-two
+// scaling.  Round-to-odd keeps both decisions exact: the exponent of the
+// maximum (a value rounded to odd never lands on a power of two it did not
+// equal) and the E2M1 rounding (24 bits rounded to odd, then to 2).
 #include "fr_device.h"
 #include "fr_launch.h"
 
@@ -50,7 +59,7 @@ __device__ __forceinline__ void st_out(void* p, u32x2 v) {
 
 // NTL / NTS: non-temporal loads of the streamed inputs / stores of the
 // outputs (the norm weight is re-read by every row and stays cached).
-template <int DT, int CPL, int MODE, bool NTL, bool NTS = NTL>
+template <int DT, int CPL, int MODE, bool NTL, bool NTS = NTL, bool MX = false>
 __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     constexpr bool ADA = MODE == M_ADA;
     constexpr bool HAS_W = MODE == M_MUL || MODE == M_ONE_PLUS;
@@ -194,6 +203,37 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
                 if (ok[k]) tmax = fmaxf(tmax, fabsf(hi));
             }
         }
+        if constexpr (MX) {
+            const float Kh = (float)rstd_d;
+            const float Kl = (float)(rstd_d - (double)Kh);
+            uint8_t* orow4 = a.out + t * (int64_t)(a.H >> 1);
+            uint8_t* srow = a.mx_scales + t * (int64_t)(a.H >> 5);
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                float q[8];
+                float m = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float p = th[k][e] * Kh;
+                    float r = fmaf(th[k][e], Kh, -p);
+                    r = fmaf(th[k][e], Kl, r);
+                    if constexpr (MODE == M_ONE_PLUS) r = fmaf(tl[k][e], Kh, r);
+                    q[e] = round_odd(p, r);
+                    m = fmaxf(m, fabsf(q[e]));
+                }
+                // a block (4 lanes) is either wholly inside the row or not
+                m = group_reduce<4>(m, OpMax());
+                const int code = mx_code(m);
+                const u32 p = pack_e2m1x8(q, mx_mult(code));
+                if (ok[k] && row_ok) {
+                    const int c = k * stride + ww * 64 + lane;
+                    u32* dst = (u32*)(orow4 + c * 4);
+                    if constexpr (NTS) __builtin_nontemporal_store(p, dst); else *dst = p;
+                    if ((lane & 3) == 0) srow[c >> 2] = (uint8_t)code;
+                }
+            }
+            return;
+        }
         double K = rstd_d * (double)a.static_scale;
         if (a.qmode == 1) {
             tmax = wave_reduce(tmax, OpMax());
@@ -230,14 +270,14 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     }
 }
 
-template <int DT, int MODE, bool NT>
+template <int DT, int MODE, bool NT, bool MX>
 static hipError_t launch_norm_mode(const NormArgs& a, int cpl, hipStream_t s) {
     const void* fn;
     switch (cpl) {
-    case 1: fn = (const void*)k_norm<DT, 1, MODE, NT>; break;
-    case 2: fn = (const void*)k_norm<DT, 2, MODE, NT>; break;
-    case 4: fn = (const void*)k_norm<DT, 4, MODE, NT>; break;
-    default: fn = (const void*)k_norm<DT, 8, MODE, NT>; break;
+    case 1: fn = (const void*)k_norm<DT, 1, MODE, NT, NT, MX>; break;
+    case 2: fn = (const void*)k_norm<DT, 2, MODE, NT, NT, MX>; break;
+    case 4: fn = (const void*)k_norm<DT, 4, MODE, NT, NT, MX>; break;
+    default: fn = (const void*)k_norm<DT, 8, MODE, NT, NT, MX>; break;
     }
     NormArgs copy = a;
     void* args[] = {&copy};
@@ -246,12 +286,19 @@ static hipError_t launch_norm_mode(const NormArgs& a, int cpl, hipStream_t s) {
 }
 
 template <int DT, bool NT>
-static hipError_t launch_norm_dt(const NormArgs& a, int mode, int cpl, hipStream_t s) {
+static hipError_t launch_norm_dt(const NormArgs& a, int mode, bool mx, int cpl, hipStream_t s) {
+    if (mx) {
+        switch (mode) {
+        case M_NONE: return launch_norm_mode<DT, M_NONE, NT, true>(a, cpl, s);
+        case M_MUL: return launch_norm_mode<DT, M_MUL, NT, true>(a, cpl, s);
+        default: return launch_norm_mode<DT, M_ONE_PLUS, NT, true>(a, cpl, s);
+        }
+    }
     switch (mode) {
-    case M_NONE: return launch_norm_mode<DT, M_NONE, NT>(a, cpl, s);
-    case M_MUL: return launch_norm_mode<DT, M_MUL, NT>(a, cpl, s);
-    case M_ONE_PLUS: return launch_norm_mode<DT, M_ONE_PLUS, NT>(a, cpl, s);
-    default: return launch_norm_mode<DT, M_ADA, NT>(a, cpl, s);
+    case M_NONE: return launch_norm_mode<DT, M_NONE, NT, false>(a, cpl, s);
+    case M_MUL: return launch_norm_mode<DT, M_MUL, NT, false>(a, cpl, s);
+    case M_ONE_PLUS: return launch_norm_mode<DT, M_ONE_PLUS, NT, false>(a, cpl, s);
+    default: return launch_norm_mode<DT, M_ADA, NT, false>(a, cpl, s);
     }
 }
 
@@ -283,17 +330,19 @@ static NormShape pick_norm_shape(int64_t T, int H, bool adaptive) {
     return {c, w, rpb, big};
 }
 
-hipError_t launch_norm(const NormArgs& in, int dtype, bool adaptive, hipStream_t s) {
+hipError_t launch_norm(const NormArgs& in, int dtype, int kind, hipStream_t s) {
     NormArgs a = in;
+    const bool adaptive = kind == NORM_ADA_FP8;
+    const bool mx = kind == NORM_MXFP4;
     const NormShape sh = pick_norm_shape(a.T, a.H, adaptive);
     a.nw = sh.nw;
     a.rpb = sh.rpb;
     const int mode = adaptive ? M_ADA : a.wmode;
     if (dtype == DT_BF16)
-        return sh.nt ? launch_norm_dt<DT_BF16, true>(a, mode, sh.cpl, s)
-                     : launch_norm_dt<DT_BF16, false>(a, mode, sh.cpl, s);
-    return sh.nt ? launch_norm_dt<DT_F16, true>(a, mode, sh.cpl, s)
-                 : launch_norm_dt<DT_F16, false>(a, mode, sh.cpl, s);
+        return sh.nt ? launch_norm_dt<DT_BF16, true>(a, mode, mx, sh.cpl, s)
+                     : launch_norm_dt<DT_BF16, false>(a, mode, mx, sh.cpl, s);
+    return sh.nt ? launch_norm_dt<DT_F16, true>(a, mode, mx, sh.cpl, s)
+                 : launch_norm_dt<DT_F16, false>(a, mode, mx, sh.cpl, s);
 }
 
 }  // namespace fr

@@ -28,7 +28,8 @@ def test_header_declares_the_four_ops_and_helpers():
     assert names == sorted([
         "fr_resid_rmsnorm_fp8", "fr_adarms_gate_res_fp8",
         "fr_qkv_normrope_kvwrite", "fr_gated_act_fp8", "fr_gemm_gated_act_fp8",
-        "fr_gemm_pack_weights", "fr_status_string", "fr_abi_version"])
+        "fr_gemm_pack_weights", "fr_resid_rmsnorm_mxfp4", "fr_gated_act_mxfp4",
+        "fr_status_string", "fr_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -195,3 +196,37 @@ def test_gemm_gated_act_validation(args, status):
 ])
 def test_gemm_pack_weights_validation(args, status):
     assert fr.lib.fr_gemm_pack_weights(*args, None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), fr.FR_ERR_NULL),
+    (dict(out_scales=None), fr.FR_ERR_NULL),
+    (dict(wmode=fr.W_MUL, weight=None), fr.FR_ERR_NULL),
+    (dict(out_fp4=E + 4), fr.FR_ERR_ALIGN),
+    (dict(H=1040), fr.FR_ERR_SHAPE),
+    (dict(H=32768 + 32), fr.FR_ERR_UNSUPPORTED),
+    (dict(wmode=3), fr.FR_ERR_MODE),
+    (dict(eps=-1.0), fr.FR_ERR_MODE),
+    (dict(dtype=7), fr.FR_ERR_DTYPE),
+    (dict(T=0), fr.FR_OK),
+])
+def test_resid_rmsnorm_mxfp4_validation(kw, status):
+    args = dict(x=A, residual=B, residual_out=C, weight=D_, wmode=fr.W_NONE,
+                eps=1e-6, out_fp4=E, out_scales=F, T=10, H=1024, dtype=fr.F16)
+    args.update(kw)
+    order = ["x", "residual", "residual_out", "weight", "wmode", "eps",
+             "out_fp4", "out_scales", "T", "H", "dtype"]
+    assert fr.lib.fr_resid_rmsnorm_mxfp4(*[args[k] for k in order], None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 0, B, C, 10, 6144, fr.BF16), fr.FR_ERR_NULL),
+    ((A, 0, B, None, 10, 6144, fr.BF16), fr.FR_ERR_NULL),
+    ((A, 3, B, C, 10, 6144, fr.BF16), fr.FR_ERR_MODE),
+    ((A, 0, B, C, 10, 6112, fr.BF16), fr.FR_ERR_SHAPE),
+    ((A, 0, B + 2, C, 10, 6144, fr.BF16), fr.FR_ERR_ALIGN),
+    ((A, 0, B, C, 10, 6144, 9), fr.FR_ERR_DTYPE),
+    ((A, 0, B, C, 0, 6144, fr.BF16), fr.FR_OK),
+])
+def test_gated_act_mxfp4_validation(args, status):
+    assert fr.lib.fr_gated_act_mxfp4(*args, None) == status
