@@ -192,6 +192,9 @@ def main():
                 for _, f in ops:
                     f(i)
         torch.cuda.synchronize()
+        run_mxfp4(torch, fr, workloads, dev, stream, 3, timed=False)
+        run_gemm_act(torch, fr, workloads, dev, stream, reps=3, timed=False,
+                     shapes=((128, 2048, 6144),))
         print(json.dumps({"pmc_pass": True, "copy_bytes_each_way": 1 << 30,
                           "op_bytes": nbytes}), flush=True)
         return
@@ -280,6 +283,9 @@ def main():
     # ---- gate_up FP8 GEMM fused with SwiGLU + block-128 FP8 --------------
     gemm = run_gemm_act(torch, fr, workloads, dev, stream)
 
+    # ---- MX FP4 producers at 8192 tokens ---------------------------------
+    mxfp4 = run_mxfp4(torch, fr, workloads, dev, stream, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
@@ -312,6 +318,7 @@ def main():
         "chain": chain,
         "decode_t10": small,
         "gemm_gated_act_fp8": gemm,
+        "mxfp4_producers": mxfp4,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
@@ -383,15 +390,19 @@ def run_chain(torch, fr, workloads, HipGraph, dev, stream, replays):
 PEAK_FP8_TFLOPS = 5000.0
 
 
-def run_gemm_act(torch, fr, workloads, dev, stream, reps=20):
+GEMM_SHAPES = ((128, 2048, 6144), (192, 2048, 6144), (1024, 2048, 6144),
+               (128, 4096, 12288), (4096, 4096, 12288))
+
+
+def run_gemm_act(torch, fr, workloads, dev, stream, reps=20, timed=True,
+                 shapes=GEMM_SHAPES):
     """The gate_up projection of the prefill FFN fused with SwiGLU and the
     block-128 FP8 output, at the Qwen3-VL 2B (hidden 2048, inter 6144) and 8B
     (hidden 4096, inter 12288) shapes.  Weights are packed once (outside the
     timing) and rotate through >= 400 MB of copies so every launch streams
     them from HBM."""
     out = {}
-    for (M, K, I) in ((128, 2048, 6144), (192, 2048, 6144), (1024, 2048, 6144),
-                      (128, 4096, 12288), (4096, 4096, 12288)):
+    for (M, K, I) in shapes:
         inp = workloads.gemm_inputs(M, K, I, 800 + M)
         a, a_s = dev(inp["a"]), dev(inp["a_scales"])
         w_raw, w_s = dev(inp["w"]), dev(inp["w_scales"])
@@ -399,7 +410,7 @@ def run_gemm_act(torch, fr, workloads, dev, stream, reps=20):
         fr.fr_gemm_pack_weights(w_raw, w0, 2 * I, K, stream=stream)
         torch.cuda.synchronize()
         del w_raw
-        nw = max(2, -(-(400 << 20) // w0.numel()))
+        nw = max(2, -(-(400 << 20) // w0.numel())) if timed else 1
         ws = [w0] + [w0.clone() for _ in range(nw - 1)]
         q = torch.empty((M, I), dtype=torch.uint8, device="cuda")
         sc = torch.empty((M, I // 128), dtype=torch.float32, device="cuda")
@@ -410,12 +421,16 @@ def run_gemm_act(torch, fr, workloads, dev, stream, reps=20):
         for i in range(3):
             f(i)
         torch.cuda.synchronize()
+        if not timed:
+            del ws, w0
+            continue
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(SPIN_CYCLES // 4)
-        e0.record(stream)
-        for i in range(reps):
-            f(i)
-        e1.record(stream)
+        with torch.cuda.stream(stream):                  # spin on the same stream
+            torch.cuda._sleep(SPIN_CYCLES // 4)
+            e0.record(stream)
+            for i in range(reps):
+                f(i)
+            e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         flops = 2.0 * M * K * 2 * I
@@ -430,6 +445,67 @@ def run_gemm_act(torch, fr, workloads, dev, stream, reps=20):
             "bound": "mfma" if flops / (PEAK_FP8_TFLOPS * 1e12) > nbytes / (PEAK_HBM_GBS * 1e9) else "hbm",
         }
         del ws, w0
+    return out
+
+
+def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
+    """The two MX FP4 producers at the bandwidth shapes (8192 tokens: RMSNorm
+    H=4096 bf16 with weight, SwiGLU I=12288 bf16), buffers rotated through
+    >= 512 MB; reps launches back to back, events at the ends."""
+    T, H, I = T_BIG, 4096, 12288
+    e = 2
+    nb_norm = T * H * 3 * e + H * e + T * H // 2 + T * H // 32
+    nb_act = T * 2 * I * e + T * I // 2 + T * I // 32
+    ri = workloads.resid_rmsnorm_inputs(T, H, workloads.BF16, 105, outliers=True)
+    gi = workloads.gated_act_inputs(T, I, workloads.BF16, 104, outliers=True)
+    N = [{k: dev(v) for k, v in ri.items()}]
+    G = [{"gu": dev(gi["gate_up"])}]
+    for lst, nb in ((N, nb_norm), (G, nb_act)):
+        for _ in range(max(2, -(-(512 << 20) // nb)) - 1 if timed else 0):
+            lst.append({k: v.clone() for k, v in lst[0].items()})
+    for d in N:
+        d["ro"] = torch.empty_like(d["x"])
+        d["q"] = torch.empty((T, H // 2), dtype=torch.uint8, device="cuda")
+        d["s"] = torch.empty((T, H // 32), dtype=torch.uint8, device="cuda")
+    for d in G:
+        d["q"] = torch.empty((T, I // 2), dtype=torch.uint8, device="cuda")
+        d["s"] = torch.empty((T, I // 32), dtype=torch.uint8, device="cuda")
+
+    def norm(i):
+        d = N[i % len(N)]
+        fr.fr_resid_rmsnorm_mxfp4(d["x"], d["residual"], d["ro"], d["weight"],
+                                  fr.W_MUL, EPS, d["q"], d["s"], T, H,
+                                  fr.BF16, stream=stream)
+
+    def act(i):
+        d = G[i % len(G)]
+        fr.fr_gated_act_mxfp4(d["gu"], fr.ACT_SWIGLU, d["q"], d["s"], T, I,
+                              fr.BF16, stream=stream)
+
+    out = {}
+    for name, f, nb in (("resid_rmsnorm_mxfp4_T8192_H4096", norm, nb_norm),
+                        ("gated_act_mxfp4_T8192_I12288", act, nb_act)):
+        for i in range(3):
+            f(i)
+        torch.cuda.synchronize()
+        if not timed:
+            continue
+        runs = []
+        with torch.cuda.stream(stream):                  # spin on the same stream
+            for _ in range(GROUP_REPEATS):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(SPIN_CYCLES)
+                e0.record(stream)
+                for i in range(reps):
+                    f(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                runs.append(e0.elapsed_time(e1) * 1e3 / reps)
+        us = float(np.median(runs))
+        out[name] = {"bytes": nb, "us_per_launch": round(us, 3),
+                     "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     return out
 
 

@@ -27,16 +27,30 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 GIB = 1 << 30
 
+ACT_FP8 = "void fr::k_act<1, 0, 8, true, false, false>"
 KERNELS = {  # kernel name prefix -> (op, algorithmic read bytes, write bytes)
-    "void fr::k_norm<1, 2, 1, true>": ("resid_rmsnorm_fp8 T=8192 H=4096 bf16 MUL TOKEN",
-                                        8192 * 4096 * 4 + 4096 * 2, 8192 * 4096 * 3 + 8192 * 4),
-    "void fr::k_norm<0, 2, 3, true>": ("adarms_gate_res_fp8 T=8192 H=1024 f16 STATIC",
-                                        8192 * 1024 * 10, 8192 * 1024 * 3),
-    "void fr::k_qkv<1, 8, true>": ("qkv_normrope_kvwrite T=8192 32/8x128 bf16",
-                                    8192 * 48 * 128 * 2 + 8192 * 4 + 512 * 4 + 512,
-                                    8192 * 48 * 128 * 2),
-    "void fr::k_act<1, 0>": ("gated_act_fp8 T=8192 I=12288 bf16 SwiGLU",
-                              8192 * 24576 * 2, 8192 * 12288 + 8192 * 96 * 4),
+    "void fr::k_norm<1, 2, 1, true, true, false>": (
+        "resid_rmsnorm_fp8 T=8192 H=4096 bf16 MUL TOKEN",
+        8192 * 4096 * 4 + 4096 * 2, 8192 * 4096 * 3 + 8192 * 4),
+    "void fr::k_norm<0, 2, 3, true, true, false>": (
+        "adarms_gate_res_fp8 T=8192 H=1024 f16 STATIC",
+        8192 * 1024 * 10, 8192 * 1024 * 3),
+    "void fr::k_qkv<1, 8, true": (
+        "qkv_normrope_kvwrite T=8192 32/8x128 bf16",
+        8192 * 48 * 128 * 2 + 8192 * 4 + 512 * 4 + 512, 8192 * 48 * 128 * 2),
+    ACT_FP8: (
+        "gated_act_fp8 T=8192 I=12288 bf16 SwiGLU",
+        8192 * 24576 * 2, 8192 * 12288 + 8192 * 96 * 4),
+    "void fr::k_norm<1, 2, 1, true, true, true>": (
+        "resid_rmsnorm_mxfp4 T=8192 H=4096 bf16 MUL",
+        8192 * 4096 * 4 + 4096 * 2, 8192 * 4096 * 2 + 8192 * 2048 + 8192 * 128),
+    "void fr::k_act<1, 0, 8, true, false, true>": (
+        "gated_act_mxfp4 T=8192 I=12288 bf16 SwiGLU",
+        8192 * 24576 * 2, 8192 * 6144 + 8192 * 384),
+    "void fr::k_gemm_act<0, 1, 2>": (
+        "gemm_gated_act_fp8 M=128 K=2048 I=6144 (weight, A, scales)",
+        12288 * 2048 + 128 * 2048 + 128 * 16 * 4 + 96 * 16 * 4,
+        128 * 6144 + 128 * 48 * 4),
 }
 
 
@@ -109,7 +123,7 @@ def pmc(fetch_db, write_db):
     with open(os.path.join(HERE, "profiles", "hbm_traffic_T8192.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
-    dom = out.get("void fr::k_act<1, 0>")
+    dom = out.get(ACT_FP8)
     if dom:
         with open(os.path.join(HERE, "memory_bound_amd", "csrc", "fr_act.hip"), "rb") as fh:
             sha = hashlib.sha256(fh.read()).hexdigest()[:16]
