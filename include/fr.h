@@ -265,6 +265,41 @@ int fr_gemm_gated_act_fp8(const uint8_t* a, const float* a_scales,
 int fr_gemm_pack_weights(const uint8_t* w, uint8_t* w_packed, int64_t N,
                          int64_t K, void* stream);
 
+/*
+ * The small-batch decoder-step chain in one persistent kernel
+ *   [FF abstract: one long-lived kernel for the forward pass at low batch;
+ *   FR 一, 三: 18 layers x 10 flow steps of gate + residual + AdaRMSNorm +
+ *   FP8, with QKV post-processing per layer, at 10 tokens]
+ *
+ *   for s in [0, steps), l in [0, layers), n = s * layers + l:
+ *     op (a'): fr_adarms_gate_res_fp8(x[l], gate[n], residual[n] ->
+ *              residual[n+1], ada_scale[n], ada_shift[n], eps, out_fp8[n],
+ *              FR_Q_STATIC, static_scale)
+ *     op (b):  fr_qkv_normrope_kvwrite(qkv[l], no q/k norm, positions,
+ *              rope_theta, rope_style, q_scale 1, q_out[l], k_cache[l],
+ *              v_cache[l], page_table, ...)
+ *   with exactly the arithmetic of those two entry points, in this order.
+ *   One launch, one workgroup; no host involvement between the ops.
+ *
+ *   x: [layers, T, H]; gate, ada_scale, ada_shift: [N, T, H]; residual:
+ *   [N+1, T, H] (slice 0 is read, slices 1..N written); out_fp8: [N, T, H]
+ *   (N = layers * steps).  qkv: [layers, T, (Hq+2Hkv)*D]; q_out:
+ *   [layers, T, Hq, D]; k_cache, v_cache: [layers, num_pages, page_size,
+ *   Hkv, D].  positions and page_table as in fr_qkv_normrope_kvwrite; an
+ *   out-of-range slot skips the token's K/V writes and sets bit 0 of
+ *   *err_flag.  T <= 32, H % 16 == 0 and H <= 1024, D % 16 == 0 and
+ *   D <= 256.  All tensors 16-byte aligned (positions, page_table,
+ *   err_flag 4-byte).
+ */
+int fr_decode_chain_persistent(
+    const void* x, const void* gate, const void* ada_scale, const void* ada_shift,
+    void* residual, uint8_t* out_fp8, float eps, float static_scale,
+    const void* qkv, const int32_t* positions, float rope_theta, int rope_style,
+    void* q_out, void* k_cache, void* v_cache, const int32_t* page_table,
+    int32_t page_table_len, int32_t page_size, int32_t num_pages,
+    int32_t* err_flag, int32_t layers, int32_t steps, int64_t T, int64_t H,
+    int32_t Hq, int32_t Hkv, int32_t D, int dtype, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fr_status_string(int status);
 

@@ -58,6 +58,10 @@ _SIGS = {
     "fr_resid_rmsnorm_mxfp4": [_P, _P, _P, _P, _INT, _F, _P, _P, _I64, _I64,
                                _INT, _P],
     "fr_gated_act_mxfp4": [_P, _INT, _P, _P, _I64, _I64, _INT, _P],
+    "fr_decode_chain_persistent": [_P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _F,
+                                   _INT, _P, _P, _P, _P, _I32, _I32, _I32, _P,
+                                   _I32, _I32, _I64, _I64, _I32, _I32, _I32,
+                                   _INT, _P],
 }
 
 
@@ -174,6 +178,20 @@ def fr_gated_act_mxfp4(gate_up, act, out_fp4, out_scales, T, I, dtype,
     _check(lib.fr_gated_act_mxfp4(
         _ptr(gate_up), act, _ptr(out_fp4), _ptr(out_scales), T, I, dtype,
         _stream(stream)))
+
+
+def fr_decode_chain_persistent(x, gate, ada_scale, ada_shift, residual,
+                               out_fp8, eps, static_scale, qkv, positions,
+                               rope_theta, rope_style, q_out, k_cache, v_cache,
+                               page_table, page_table_len, page_size, num_pages,
+                               err_flag, layers, steps, T, H, Hq, Hkv, D, dtype,
+                               stream=None):
+    _check(lib.fr_decode_chain_persistent(
+        _ptr(x), _ptr(gate), _ptr(ada_scale), _ptr(ada_shift), _ptr(residual),
+        _ptr(out_fp8), eps, static_scale, _ptr(qkv), _ptr(positions),
+        rope_theta, rope_style, _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
+        _ptr(page_table), page_table_len, page_size, num_pages, _ptr(err_flag),
+        layers, steps, T, H, Hq, Hkv, D, dtype, _stream(stream)))
 
 
 def fr_gemm_gated_act_fp8(a, a_scales, w_packed, w_scales, act, out_fp8,

@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfrhip.so")
-SOURCES = ["fr_api.hip", "fr_norm.hip", "fr_qkv.hip", "fr_act.hip", "fr_gemm.hip"]
+SOURCES = ["fr_api.hip", "fr_norm.hip", "fr_qkv.hip", "fr_act.hip", "fr_gemm.hip",
+           "fr_chain.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

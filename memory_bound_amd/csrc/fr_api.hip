@@ -280,6 +280,66 @@ FR_EXPORT int fr_gemm_pack_weights(const uint8_t* w, uint8_t* w_packed, int64_t 
     return launch_status(fr::launch_pack_w(p, (hipStream_t)stream));
 }
 
+FR_EXPORT int fr_decode_chain_persistent(
+    const void* x, const void* gate, const void* ada_scale, const void* ada_shift,
+    void* residual, uint8_t* out_fp8, float eps, float static_scale,
+    const void* qkv, const int32_t* positions, float rope_theta, int rope_style,
+    void* q_out, void* k_cache, void* v_cache, const int32_t* page_table,
+    int32_t page_table_len, int32_t page_size, int32_t num_pages,
+    int32_t* err_flag, int32_t layers, int32_t steps, int64_t T, int64_t H,
+    int32_t Hq, int32_t Hkv, int32_t D, int dtype, void* stream) {
+    if (dtype != FR_F16 && dtype != FR_BF16) return FR_ERR_DTYPE;
+    if (layers <= 0 || steps <= 0 || T < 0 || H <= 0 || H % 16 != 0) return FR_ERR_SHAPE;
+    if (Hq <= 0 || Hkv <= 0 || D <= 0 || D % 16 != 0) return FR_ERR_SHAPE;
+    if (page_table_len <= 0 || page_size <= 0 || num_pages <= 0) return FR_ERR_SHAPE;
+    if (T > fr::kChainMaxT || H > fr::kChainMaxH || D > 256) return FR_ERR_UNSUPPORTED;
+    if ((int64_t)layers * steps > (1LL << 24)) return FR_ERR_UNSUPPORTED;
+    if ((int64_t)Hq + 2 * (int64_t)Hkv > 65536) return FR_ERR_UNSUPPORTED;
+    if (rope_style != FR_ROPE_HALF && rope_style != FR_ROPE_INTERLEAVED) return FR_ERR_MODE;
+    if (!finite_nonneg(eps)) return FR_ERR_MODE;
+    if (!(isfinite(static_scale) && static_scale > 0.0f)) return FR_ERR_MODE;
+    if (!(isfinite(rope_theta) && rope_theta > 1.0f)) return FR_ERR_MODE;
+    if (!x || !gate || !ada_scale || !ada_shift || !residual || !out_fp8 || !qkv ||
+        !positions || !q_out || !k_cache || !v_cache || !page_table)
+        return FR_ERR_NULL;
+    if (!aligned16(x) || !aligned16(gate) || !aligned16(ada_scale) || !aligned16(ada_shift) ||
+        !aligned16(residual) || !aligned16(out_fp8) || !aligned16(qkv) || !aligned16(q_out) ||
+        !aligned16(k_cache) || !aligned16(v_cache))
+        return FR_ERR_ALIGN;
+    if (!aligned4(positions) || !aligned4(page_table) || (err_flag && !aligned4(err_flag)))
+        return FR_ERR_ALIGN;
+    if (T == 0) return FR_OK;
+    fr::ChainArgs a{};
+    a.x = x;
+    a.gate = gate;
+    a.ada_scale = ada_scale;
+    a.ada_shift = ada_shift;
+    a.res = residual;
+    a.out = out_fp8;
+    a.qkv = qkv;
+    a.pos = positions;
+    a.table = page_table;
+    a.q_out = q_out;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.err = err_flag;
+    a.layers = layers;
+    a.steps = steps;
+    a.T = (int)T;
+    a.H = (int)H;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.table_len = page_table_len;
+    a.page_size = page_size;
+    a.num_pages = num_pages;
+    a.style = rope_style;
+    a.eps = eps;
+    a.static_scale = static_scale;
+    a.theta = rope_theta;
+    return launch_status(fr::launch_chain(a, dtype, (hipStream_t)stream));
+}
+
 FR_EXPORT const char* fr_status_string(int status) {
     switch (status) {
     case FR_OK: return "FR_OK";

@@ -253,6 +253,42 @@ __device__ __forceinline__ u32 pack_e2m1x4(float a, float b, float c, float d, f
     return p;
 }
 
+// sin and cos of x (radians).  k = nearest integer to x/(pi/2), r = x - k*pi/2
+// with pi/2 split into a head (the double nearest pi/2) and its tail; fma
+// keeps k*head exact.  Taylor series to r^11 / r^12 (truncation < 1e-11 on
+// |r| <= pi/4), then the quadrant of k picks and signs the two.
+__device__ __forceinline__ void sincos_pos(double x, float* s_out, float* c_out) {
+    const double two_over_pi = 0.63661977236758134308;
+    const double pio2_hi = 1.5707963267948966;          // nearest double to pi/2
+    const double pio2_lo = 6.123233995736766e-17;       // pi/2 - pio2_hi
+    const double k = rint(x * two_over_pi);
+    double r = fma(-k, pio2_hi, x);
+    r = fma(-k, pio2_lo, r);
+    const double r2 = r * r;
+    // 1/n! coefficients
+    double sp = 2.505210838544172e-08;                  // 1/11!
+    sp = fma(sp, r2, -2.7557319223985893e-06);          // 1/9!
+    sp = fma(sp, r2, 1.984126984126984e-04);            // 1/7!
+    sp = fma(sp, r2, -8.333333333333333e-03);           // 1/5!
+    sp = fma(sp, r2, 1.6666666666666666e-01);           // 1/3!
+    const double sn = fma(-r * r2, sp, r);
+    double cp = 2.08767569878681e-09;                   // 1/12!
+    cp = fma(cp, r2, -2.755731922398589e-07);           // 1/10!
+    cp = fma(cp, r2, 2.48015873015873e-05);             // 1/8!
+    cp = fma(cp, r2, -1.388888888888889e-03);           // 1/6!
+    cp = fma(cp, r2, 4.1666666666666664e-02);           // 1/4!
+    cp = fma(cp, r2, -0.5);                             // 1/2!
+    const double cs = fma(cp, r2, 1.0);
+    const int q = (int)((long long)k & 3);
+    double s, c;
+    if (q == 0) { s = sn; c = cs; }
+    else if (q == 1) { s = cs; c = -sn; }
+    else if (q == 2) { s = -sn; c = -cs; }
+    else { s = -cs; c = sn; }
+    *s_out = (float)s;
+    *c_out = (float)c;
+}
+
 __device__ __forceinline__ u32x4 ld128(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }

@@ -91,6 +91,32 @@ struct PackArgs {
     int64_t units;          // N * K / 16
 };
 
+// The decoder-step chain (op a' then op b per layer and flow step) in one
+// persistent workgroup.
+constexpr int kChainWaves = 16;
+constexpr int kChainMaxT = 2 * kChainWaves;     // two rows per wave
+constexpr int kChainMaxH = 2 * 64 * 8;          // two 8-value chunks per lane
+struct ChainArgs {
+    const void* x;          // [layers, T, H]
+    const void* gate;       // [N, T, H]  (N = layers * steps)
+    const void* ada_scale;  // [N, T, H]
+    const void* ada_shift;  // [N, T, H]
+    void* res;              // [N + 1, T, H]
+    uint8_t* out;           // [N, T, H]
+    const void* qkv;        // [layers, T, (Hq + 2 Hkv) D]
+    const int32_t* pos;     // [T]
+    const int32_t* table;
+    void* q_out;            // [layers, T, Hq, D]
+    void* kc;               // [layers, pages, page_size, Hkv, D]
+    void* vc;
+    int32_t* err;
+    int layers, steps, T, H, Hq, Hkv, D;
+    int table_len, page_size, num_pages;
+    int style;
+    float eps, static_scale, theta;
+};
+hipError_t launch_chain(const ChainArgs& a, int dtype, hipStream_t s);
+
 enum { NORM_FP8 = 0, NORM_ADA_FP8 = 1, NORM_MXFP4 = 2 };
 hipError_t launch_norm(const NormArgs& a, int dtype, int kind, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int dtype, hipStream_t s);

@@ -29,7 +29,7 @@ def test_header_declares_the_four_ops_and_helpers():
         "fr_resid_rmsnorm_fp8", "fr_adarms_gate_res_fp8",
         "fr_qkv_normrope_kvwrite", "fr_gated_act_fp8", "fr_gemm_gated_act_fp8",
         "fr_gemm_pack_weights", "fr_resid_rmsnorm_mxfp4", "fr_gated_act_mxfp4",
-        "fr_status_string", "fr_abi_version"])
+        "fr_decode_chain_persistent", "fr_status_string", "fr_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -230,3 +230,37 @@ def test_resid_rmsnorm_mxfp4_validation(kw, status):
 ])
 def test_gated_act_mxfp4_validation(args, status):
     assert fr.lib.fr_gated_act_mxfp4(*args, None) == status
+
+
+def chain(**kw):
+    args = dict(x=A, gate=B, ada_scale=C, ada_shift=D_, residual=E, out_fp8=F,
+                eps=1e-6, static_scale=56.0, qkv=G, positions=A, rope_theta=1e4,
+                rope_style=fr.ROPE_HALF, q_out=B, k_cache=C, v_cache=D_,
+                page_table=E, page_table_len=1, page_size=1024, num_pages=1,
+                err_flag=None, layers=18, steps=10, T=10, H=1024, Hq=8, Hkv=1,
+                D=256, dtype=fr.F16)
+    args.update(kw)
+    order = ["x", "gate", "ada_scale", "ada_shift", "residual", "out_fp8", "eps",
+             "static_scale", "qkv", "positions", "rope_theta", "rope_style",
+             "q_out", "k_cache", "v_cache", "page_table", "page_table_len",
+             "page_size", "num_pages", "err_flag", "layers", "steps", "T", "H",
+             "Hq", "Hkv", "D", "dtype"]
+    return fr.lib.fr_decode_chain_persistent(*[args[k] for k in order], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), fr.FR_ERR_NULL),
+    (dict(page_table=None), fr.FR_ERR_NULL),
+    (dict(T=33), fr.FR_ERR_UNSUPPORTED),
+    (dict(H=2048), fr.FR_ERR_UNSUPPORTED),
+    (dict(D=512), fr.FR_ERR_UNSUPPORTED),
+    (dict(H=1000), fr.FR_ERR_SHAPE),
+    (dict(layers=0), fr.FR_ERR_SHAPE),
+    (dict(static_scale=0.0), fr.FR_ERR_MODE),
+    (dict(rope_style=5), fr.FR_ERR_MODE),
+    (dict(q_out=B + 8), fr.FR_ERR_ALIGN),
+    (dict(dtype=3), fr.FR_ERR_DTYPE),
+    (dict(T=0), fr.FR_OK),
+])
+def test_decode_chain_persistent_validation(kw, status):
+    assert chain(**kw) == status

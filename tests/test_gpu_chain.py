@@ -123,3 +123,84 @@ def test_decode_chain_eager_and_graph():
         graph.launch()
         stream.synchronize()
         compare(chain.host(), want)
+
+
+def test_decode_chain_persistent_kernel():
+    """The same 360 ops in one persistent launch, against the oracle; run
+    twice with poisoned outputs in between (the second run must match too)."""
+    import memory_bound_amd as fr
+    announce("decode chain: persistent kernel")
+    ci = workloads.chain_inputs()
+    want = oracle_chain(ci)
+    stream = torch.cuda.Stream()
+    ch = DeviceChain(fr, ci, stream)
+    d = ch.d
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        ch.poison()
+        ch.kc.copy_(to_dev(ci["k_cache"]))
+        ch.vc.copy_(to_dev(ci["v_cache"]))
+        fr.fr_decode_chain_persistent(
+            ch.x, ch.gate, ch.sc, ch.sh, ch.res, ch.q8, EPS, 56.0, ch.qkv,
+            ch.pos, THETA, fr.ROPE_HALF, ch.q_out, ch.kc, ch.vc, ch.table, 1,
+            d["page_size"], 1, err, d["layers"], d["steps"], d["T"], d["H"],
+            d["Hq"], d["Hkv"], d["D"], fr.F16, stream=stream)
+        stream.synchronize()
+        compare(ch.host(), want)
+        assert int(err.item()) == 0
+
+
+def test_decode_chain_persistent_small_bf16_interleaved():
+    """A smaller chain in bf16 with interleaved RoPE, 3 KV heads, 17 tokens
+    (two rows per wave for some waves) and a paged table of 4 pages."""
+    import memory_bound_amd as fr
+    announce("decode chain persistent: bf16, interleaved, T=17")
+    rng = np.random.default_rng(909)
+    L, S, T, H, Hq, Hkv, D, P, pages = 3, 2, 17, 512, 4, 3, 64, 8, 4
+    BF = 1
+    N = L * S
+    x = workloads.to16(rng.standard_normal((L, T, H), dtype=np.float32), BF)
+    gate = workloads.to16(0.1 * rng.standard_normal((N, T, H), dtype=np.float32), BF)
+    sc = workloads.to16(0.1 * rng.standard_normal((N, T, H), dtype=np.float32), BF)
+    sh = workloads.to16(0.1 * rng.standard_normal((N, T, H), dtype=np.float32), BF)
+    r0 = workloads.to16(rng.standard_normal((T, H), dtype=np.float32), BF)
+    qkv = workloads.to16(rng.standard_normal((L, T, (Hq + 2 * Hkv) * D), dtype=np.float32), BF)
+    pos = np.arange(5, 5 + T, dtype=np.int32)
+    table = rng.permutation(pages).astype(np.int32)
+    kc0 = np.full((L, pages, P, Hkv, D), workloads.SENTINEL, np.uint16)
+    vc0 = kc0.copy()
+    # oracle
+    res = np.empty((N + 1, T, H), np.uint16)
+    res[0] = r0
+    q8 = np.empty((N, T, H), np.uint8)
+    qo = np.empty((L, T, Hq, D), np.uint16)
+    kc, vc = kc0.copy(), vc0.copy()
+    n = 0
+    for s in range(S):
+        for l in range(L):
+            res[n + 1], q8[n], _ = oracle.adarms_gate_res_fp8(
+                x[l], gate[n], res[n], sc[n], sh[n], EPS, oracle.Q_STATIC, 40.0, BF)
+            qo[l], err = oracle.qkv_normrope_kvwrite(
+                qkv[l], None, None, EPS, pos, 5e5, oracle.ROPE_INTERLEAVED,
+                kc[l], vc[l], table, P, Hq, Hkv, D, BF)
+            assert err == 0
+            n += 1
+    # device
+    dres = torch.full((N + 1, T, H), 0x7E01, dtype=torch.int16, device="cuda")
+    dres[0] = to_dev(r0)
+    dq8 = torch.full((N, T, H), 0x7F, dtype=torch.uint8, device="cuda")
+    dqo = torch.full((L, T, Hq, D), 0x7E01, dtype=torch.int16, device="cuda")
+    dkc, dvc = to_dev(kc0), to_dev(vc0)
+    fr.fr_decode_chain_persistent(
+        to_dev(x), to_dev(gate), to_dev(sc), to_dev(sh), dres, dq8, EPS, 40.0,
+        to_dev(qkv), to_dev(pos), 5e5, fr.ROPE_INTERLEAVED, dqo, dkc, dvc,
+        to_dev(table), pages, P, pages, None, L, S, T, H, Hq, Hkv, D, BF)
+    torch.cuda.synchronize()
+    check_exact(to_host(dres, np.uint16), res, "residual chain")
+    check_fp8(to_host(dq8, np.uint8), q8, "fp8 outputs")
+    check16(to_host(dqo, np.uint16), qo, BF, "q_out")
+    kg = to_host(dkc, np.uint16)
+    written = kc != workloads.SENTINEL
+    check_exact(kg[~written], kc[~written], "k_cache untouched")
+    check16(kg[written], kc[written], BF, "k_cache")
+    check_exact(to_host(dvc, np.uint16), vc, "v_cache")
