@@ -279,7 +279,8 @@ int fr_gemm_pack_weights(const uint8_t* w, uint8_t* w_packed, int64_t N,
  *              rope_theta, rope_style, q_scale 1, q_out[l], k_cache[l],
  *              v_cache[l], page_table, ...)
  *   with exactly the arithmetic of those two entry points, in this order.
- *   One launch, one workgroup; no host involvement between the ops.
+ *   One launch; no host involvement and no synchronisation between the
+ *   ops (each output location is owned by one wave for the whole chain).
  *
  *   x: [layers, T, H]; gate, ada_scale, ada_shift: [N, T, H]; residual:
  *   [N+1, T, H] (slice 0 is read, slices 1..N written); out_fp8: [N, T, H]
@@ -287,7 +288,7 @@ int fr_gemm_pack_weights(const uint8_t* w, uint8_t* w_packed, int64_t N,
  *   [layers, T, Hq, D]; k_cache, v_cache: [layers, num_pages, page_size,
  *   Hkv, D].  positions and page_table as in fr_qkv_normrope_kvwrite; an
  *   out-of-range slot skips the token's K/V writes and sets bit 0 of
- *   *err_flag.  T <= 32, H % 16 == 0 and H <= 1024, D % 16 == 0 and
+ *   *err_flag.  T <= 64, H % 16 == 0 and H <= 1024, D % 16 == 0 and
  *   D <= 256.  All tensors 16-byte aligned (positions, page_table,
  *   err_flag 4-byte).
  */

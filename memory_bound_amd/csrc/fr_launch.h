@@ -92,9 +92,8 @@ struct PackArgs {
 };
 
 // The decoder-step chain (op a' then op b per layer and flow step) in one
-// persistent workgroup.
-constexpr int kChainWaves = 16;
-constexpr int kChainMaxT = 2 * kChainWaves;     // two rows per wave
+// persistent launch: one wave per token row, further waves per head units.
+constexpr int kChainMaxT = 64;
 constexpr int kChainMaxH = 2 * 64 * 8;          // two 8-value chunks per lane
 struct ChainArgs {
     const void* x;          // [layers, T, H]

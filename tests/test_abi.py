@@ -251,7 +251,7 @@ def chain(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), fr.FR_ERR_NULL),
     (dict(page_table=None), fr.FR_ERR_NULL),
-    (dict(T=33), fr.FR_ERR_UNSUPPORTED),
+    (dict(T=65), fr.FR_ERR_UNSUPPORTED),
     (dict(H=2048), fr.FR_ERR_UNSUPPORTED),
     (dict(D=512), fr.FR_ERR_UNSUPPORTED),
     (dict(H=1000), fr.FR_ERR_SHAPE),
