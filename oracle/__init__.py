@@ -97,6 +97,14 @@ def lib():
         L.oracle_resid_rmsnorm_mxfp4.restype = _INT
         L.oracle_gated_act_mxfp4.argtypes = [_P, _INT, _P, _P, _I64, _I64, _INT]
         L.oracle_gated_act_mxfp4.restype = _INT
+        L.or_layernorm.argtypes = [_P, _P, _P, _I64, _D, _P]
+        L.or_layernorm.restype = None
+        L.or_rope3d.argtypes = [_P, _I64, _P, _P, _D, _INT]
+        L.or_rope3d.restype = None
+        L.oracle_qk_norm_rope.argtypes = [
+            _P, _INT, _INT, _P, _P, _P, _P, _F, _P, _INT, _P, _F, _INT, _F,
+            _P, _P, _P, _I64, _I32, _I32, _I32, _INT]
+        L.oracle_qk_norm_rope.restype = _INT
         L.oracle_resid_rmsnorm_fp8.argtypes = [
             _P, _P, _P, _P, _INT, _F, _P, _INT, _F, _P, _I64, _I64, _INT]
         L.oracle_adarms_gate_res_fp8.argtypes = [
@@ -371,6 +379,47 @@ def gated_act_mxfp4(gate_up, act_kind, dtype):
                                       _ptr(sc), T, I, dtype)
     assert rc == 0
     return q, sc
+
+
+NORM_NONE, NORM_RMS, NORM_LAYER = 0, 1, 2
+SCOPE_HEAD, SCOPE_FULL = 0, 1
+
+
+def layernorm(v, w=None, b=None, eps=1e-6):
+    v = _c(v, np.float64)
+    w = _c(w, np.float64) if w is not None else None
+    b = _c(b, np.float64) if b is not None else None
+    y = np.empty_like(v)
+    lib().or_layernorm(_ptr(v), _ptr(w), _ptr(b), v.size, float(eps), _ptr(y))
+    return y
+
+
+def rope3d(v, pos3, sections, theta, style=ROPE_HALF):
+    v = _c(v, np.float64).copy()
+    p = np.ascontiguousarray(pos3, dtype=np.int32)
+    sec = np.ascontiguousarray(sections, dtype=np.int32)
+    lib().or_rope3d(_ptr(v), v.size, _ptr(p), _ptr(sec), float(theta), style)
+    return v
+
+
+def qk_norm_rope(qkv, norm_kind, norm_scope, q_norm_w, q_norm_b, k_norm_w,
+                 k_norm_b, eps, positions, rope_dims, sections, rope_theta,
+                 rope_style, q_scale, Hq, Hkv, D, dtype):
+    """Returns (q_out [T,Hq,D], k_out [T,Hkv,D], v_out [T,Hkv,D]) uint16."""
+    qkv = _c(qkv, np.uint16)
+    T = qkv.shape[0]
+    ws = [_c(a, np.uint16) for a in (q_norm_w, q_norm_b, k_norm_w, k_norm_b)]
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    sec = np.ascontiguousarray(sections, dtype=np.int32) if sections is not None else None
+    q = np.empty((T, Hq, D), np.uint16)
+    k = np.empty((T, Hkv, D), np.uint16)
+    v = np.empty((T, Hkv, D), np.uint16)
+    rc = lib().oracle_qk_norm_rope(
+        _ptr(qkv), norm_kind, norm_scope, *[_ptr(a) for a in ws], eps, _ptr(pos),
+        rope_dims, _ptr(sec), rope_theta, rope_style, q_scale, _ptr(q), _ptr(k),
+        _ptr(v), T, Hq, Hkv, D, dtype)
+    assert rc == 0
+    return q, k, v
 
 
 def gated_act_fp8_f64(gate_up, act_kind):

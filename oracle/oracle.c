@@ -229,6 +229,49 @@ void or_rope(double* v, int64_t D, int64_t pos, double theta, int style)
     }
 }
 
+/* LayerNorm [FR section 2.2: the Chameleon prefill path normalises Q and K
+ * with LayerNorm]: y = (v - mean) / sqrt(var + eps) * w + b with the mean
+ * and the (biased) variance over the n values; w = 1 and b = 0 when NULL. */
+void or_layernorm(const double* v, const double* w, const double* b,
+                  int64_t n, double eps, double* y)
+{
+    double mean = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        mean += v[j];
+    mean /= (double)n;
+    double var = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        var += (v[j] - mean) * (v[j] - mean);
+    var /= (double)n;
+    double rstd = 1.0 / sqrt(var + eps);
+    for (int64_t j = 0; j < n; ++j)
+        y[j] = (v[j] - mean) * rstd * (w ? w[j] : 1.0) + (b ? b[j] : 0.0);
+}
+
+/* 3D RoPE [FR section 2.2: the Wan video path rotates Q and K with a 3D
+ * RoPE].  The D/2 rotary pairs are split into three consecutive ranges of
+ * sec[0], sec[1], sec[2] pairs (time, height, width; the sum is D/2); pair
+ * i of range a, at local index k, turns by pos3[a] * theta^(-k / sec[a]),
+ * i.e. each range is a 1D RoPE of width 2 sec[a] on its own axis.  Pairs
+ * are (i, i + D/2) or (2i, 2i+1) as in or_rope. */
+void or_rope3d(double* v, int64_t D, const int32_t* pos3, const int32_t* sec,
+               double theta, int style)
+{
+    int64_t half = D / 2;
+    for (int64_t i = 0; i < half; ++i) {
+        int a = i < sec[0] ? 0 : (i < sec[0] + sec[1] ? 1 : 2);
+        int64_t k = i - (a > 0 ? sec[0] : 0) - (a > 1 ? sec[1] : 0);
+        double inv_freq = pow(theta, -(double)k / (double)sec[a]);
+        double ang = (double)pos3[a] * inv_freq;
+        double c = cos(ang), s = sin(ang);
+        int64_t ia = style == OR_ROPE_INTERLEAVED ? 2 * i : i;
+        int64_t ib = style == OR_ROPE_INTERLEAVED ? 2 * i + 1 : i + half;
+        double x0 = v[ia], x1 = v[ib];
+        v[ia] = x0 * c - x1 * s;
+        v[ib] = x1 * c + x0 * s;
+    }
+}
+
 /* Gate activations: SiLU (SwiGLU) [SM89 Phase 2], GELU with the tanh
  * approximation (GeGLU) [FR section 二 table, steps 8-10] and squared ReLU
  * [FP, third technique]. */
@@ -575,6 +618,88 @@ int oracle_gated_act_fp8_f64(const double* gate_up, int act, uint8_t* out_fp8,
                 or_quant_dynamic(h, B, out_fp8 + t * I + b * B);
         }
     }
+    return 0;
+}
+
+/* Packed QKV split + Q/K norm + RoPE, the common contract of the Q/K
+ * post-processing variants [FR section 2.2: one kernel normalises Q and K
+ * and rotates them, V passes through; the variants differ in the norm
+ * (RMSNorm, or LayerNorm on the Chameleon path), its scope (per head, or
+ * the full width of all Q and all K heads on the Wan path) and the RoPE
+ * layout (1D, or 3D on the Wan path)].
+ *   row t of qkv = [Q heads | K heads | V heads], each head D-contiguous.
+ *   norm (Q and K separately): per head over D with weight / bias [D], or
+ *   over all Hq*D (Hkv*D) values with weight / bias [Hq*D] ([Hkv*D]);
+ *   NULL weight = 1, NULL bias = 0; RMSNorm takes no bias.
+ *   RoPE per head at positions[t] (1D) or positions[3t..3t+2] (3D, with
+ *   sections[3] pairs per axis); Q times q_scale; one rounding.
+ *   q_out [T,Hq,D], k_out [T,Hkv,D], v_out [T,Hkv,D] (V copied bit for bit). */
+int oracle_qk_norm_rope(const uint16_t* qkv, int norm_kind, int norm_scope,
+                        const uint16_t* q_norm_w, const uint16_t* q_norm_b,
+                        const uint16_t* k_norm_w, const uint16_t* k_norm_b,
+                        float eps, const int32_t* positions, int rope_dims,
+                        const int32_t* sections, float rope_theta, int rope_style,
+                        float q_scale, uint16_t* q_out, uint16_t* k_out,
+                        uint16_t* v_out, int64_t T, int32_t Hq, int32_t Hkv,
+                        int32_t D, int dtype)
+{
+    int64_t NH = Hq + 2 * Hkv, row = NH * D;
+    int64_t nq = (int64_t)Hq * D, nk = (int64_t)Hkv * D;
+    int64_t wq = norm_scope == OR_SCOPE_FULL ? nq : D;
+    int64_t wk = norm_scope == OR_SCOPE_FULL ? nk : D;
+    double* v = malloc(sizeof(double) * (size_t)row);
+    double* y = malloc(sizeof(double) * (size_t)row);
+    double* w4 = malloc(sizeof(double) * (size_t)(2 * (wq + wk)));
+    if (!v || !y || !w4) {
+        free(v); free(y); free(w4);
+        return -1;
+    }
+    double* qw = w4;
+    double* qb = w4 + wq;
+    double* kw = w4 + 2 * wq;
+    double* kb = w4 + 2 * wq + wk;
+    for (int64_t j = 0; j < wq; ++j) {
+        qw[j] = q_norm_w ? dec16(q_norm_w[j], dtype) : 1.0;
+        qb[j] = q_norm_b ? dec16(q_norm_b[j], dtype) : 0.0;
+    }
+    for (int64_t j = 0; j < wk; ++j) {
+        kw[j] = k_norm_w ? dec16(k_norm_w[j], dtype) : 1.0;
+        kb[j] = k_norm_b ? dec16(k_norm_b[j], dtype) : 0.0;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t j = 0; j < row; ++j)
+            v[j] = dec16(qkv[t * row + j], dtype);
+        memcpy(y, v, sizeof(double) * (size_t)row);
+        /* norm of Q (values [0, nq)) and of K ([nq, nq + nk)) */
+        for (int part = 0; part < 2; ++part) {
+            int64_t base = part == 0 ? 0 : nq;
+            int64_t len = part == 0 ? nq : nk;
+            int64_t span = norm_scope == OR_SCOPE_FULL ? len : D;
+            const double* w = part == 0 ? qw : kw;
+            const double* b = part == 0 ? qb : kb;
+            if (norm_kind == OR_NORM_NONE)
+                continue;
+            for (int64_t o = 0; o < len; o += span) {
+                if (norm_kind == OR_NORM_RMS)
+                    or_rmsnorm(v + base + o, w, OR_W_MUL, span, (double)eps, y + base + o);
+                else
+                    or_layernorm(v + base + o, w, b, span, (double)eps, y + base + o);
+            }
+        }
+        /* RoPE per Q / K head, Q pre-scale, one rounding */
+        for (int64_t h = 0; h < Hq + Hkv; ++h) {
+            double* yh = y + h * D;
+            if (rope_dims == 3)
+                or_rope3d(yh, D, positions + 3 * t, sections, (double)rope_theta, rope_style);
+            else
+                or_rope(yh, D, positions[t], (double)rope_theta, rope_style);
+            uint16_t* dst = h < Hq ? q_out + (t * Hq + h) * D : k_out + (t * Hkv + (h - Hq)) * D;
+            for (int64_t d = 0; d < D; ++d)
+                dst[d] = enc16(h < Hq ? yh[d] * (double)q_scale : yh[d], dtype);
+        }
+        memcpy(v_out + t * nk, qkv + t * row + nq + nk, sizeof(uint16_t) * (size_t)nk);
+    }
+    free(v); free(y); free(w4);
     return 0;
 }
 

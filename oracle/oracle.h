@@ -39,6 +39,8 @@ enum { OR_Q_STATIC = 0, OR_Q_TOKEN = 1 };
 enum { OR_ACT_SWIGLU = 0, OR_ACT_GEGLU_TANH = 1, OR_ACT_SQRELU = 2 };
 /* RoPE pairing */
 enum { OR_ROPE_HALF = 0, OR_ROPE_INTERLEAVED = 1 };
+enum { OR_NORM_NONE = 0, OR_NORM_RMS = 1, OR_NORM_LAYER = 2 };
+enum { OR_SCOPE_HEAD = 0, OR_SCOPE_FULL = 1 };
 
 /* ---- number formats ---- */
 double   or_f16_decode(uint16_t bits);
@@ -59,6 +61,10 @@ void   or_rmsnorm(const double* v, const double* w, int wmode, int64_t n,
 void   or_adarms(const double* h, const double* scale, const double* shift,
                  int64_t n, double eps, double* y);
 void   or_rope(double* v, int64_t D, int64_t pos, double theta, int style);
+void   or_layernorm(const double* v, const double* w, const double* b,
+                    int64_t n, double eps, double* y);   /* w, b may be NULL */
+void   or_rope3d(double* v, int64_t D, const int32_t* pos3, const int32_t* sec,
+                 double theta, int style);
 double or_act(double g, int act);
 void   or_quant_static(const double* y, int64_t n, double mult, uint8_t* q);
 float  or_quant_dynamic(const double* y, int64_t n, uint8_t* q);
@@ -103,6 +109,14 @@ int oracle_resid_rmsnorm_mxfp4(const uint16_t* x, const uint16_t* residual,
                                int dtype);
 int oracle_gated_act_mxfp4(const uint16_t* gate_up, int act, uint8_t* out_fp4,
                            uint8_t* out_scales, int64_t T, int64_t I, int dtype);
+int oracle_qk_norm_rope(const uint16_t* qkv, int norm_kind, int norm_scope,
+                        const uint16_t* q_norm_w, const uint16_t* q_norm_b,
+                        const uint16_t* k_norm_w, const uint16_t* k_norm_b,
+                        float eps, const int32_t* positions, int rope_dims,
+                        const int32_t* sections, float rope_theta, int rope_style,
+                        float q_scale, uint16_t* q_out, uint16_t* k_out,
+                        uint16_t* v_out, int64_t T, int32_t Hq, int32_t Hkv,
+                        int32_t D, int dtype);
 int oracle_gated_act_fp8_f64(const double* gate_up, int act, uint8_t* out_fp8,
                              float* out_scales, int64_t T, int64_t I);
 
