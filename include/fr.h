@@ -82,6 +82,10 @@ typedef enum { FR_ACT_SWIGLU = 0, FR_ACT_GEGLU_TANH = 1, FR_ACT_SQRELU = 2 } fr_
  * element 2i with 2i+1. */
 typedef enum { FR_ROPE_HALF = 0, FR_ROPE_INTERLEAVED = 1 } fr_rope;
 
+/* Q/K norm of fr_qk_norm_rope: kind and scope ([FR 2.2]). */
+typedef enum { FR_NORM_NONE = 0, FR_NORM_RMS = 1, FR_NORM_LAYER = 2 } fr_norm_kind;
+typedef enum { FR_SCOPE_HEAD = 0, FR_SCOPE_FULL = 1 } fr_norm_scope;
+
 /*
  * (a) Residual add + RMSNorm + FP8 quantisation  [FR 二 table step 1, 2.1]
  *
@@ -300,6 +304,39 @@ int fr_decode_chain_persistent(
     int32_t page_table_len, int32_t page_size, int32_t num_pages,
     int32_t* err_flag, int32_t layers, int32_t steps, int64_t T, int64_t H,
     int32_t Hq, int32_t Hkv, int32_t D, int dtype, void* stream);
+
+/*
+ * (b-var) Packed-QKV split + Q/K norm + RoPE into separate Q, K, V outputs:
+ *     the variants of op (b)'s contract [FR 2.2: Q and K normalised, then
+ *     rotated, V passed through; the Chameleon prefill path uses LayerNorm
+ *     per head with rotate-half RoPE; the Wan video path normalises over the
+ *     full width and applies a 3D RoPE; HY 04 step 10 for q_scale]
+ *
+ *   norm_kind: FR_NORM_NONE, FR_NORM_RMS (v * rstd * w), FR_NORM_LAYER
+ *     ((v - mean) * rstd * w + b, biased variance); rstd = 1/sqrt(. + eps).
+ *   norm_scope: FR_SCOPE_HEAD (per head over D; w, b: [D] shared by all
+ *     heads) or FR_SCOPE_FULL (over all Hq*D Q values, and separately all
+ *     Hkv*D K values; w, b: [Hq*D] and [Hkv*D]).  NULL weight = 1, NULL
+ *     bias = 0; RMSNorm ignores the bias.
+ *   rope_dims 1: pair i (0 <= i < D/2) turns by positions[t] *
+ *     rope_theta^(-2i/D).  rope_dims 3: positions is [T,3] (time, height,
+ *     width); the pairs split into ranges of sec_t, sec_h, sec_w pairs
+ *     (each >= 1, sum D/2); pair k of range a turns by positions[t,a] *
+ *     rope_theta^(-k / sec_a).  rope_style: FR_ROPE_HALF pairs (i, i+D/2),
+ *     FR_ROPE_INTERLEAVED (2i, 2i+1).
+ *   Q is multiplied by q_scale after RoPE; one rounding per output value.
+ *   qkv: [T,(Hq+2Hkv)*D]; q_out: [T,Hq,D]; k_out, v_out: [T,Hkv,D] (V copied
+ *   bit for bit).  D % 16 == 0, D <= 256, (Hq+2Hkv) * p <= 1024 with p the
+ *   power of two >= D/16.  Tensors 16-byte aligned, positions 4-byte.
+ */
+int fr_qk_norm_rope(const void* qkv, int norm_kind, int norm_scope,
+                    const void* q_norm_w, const void* q_norm_b,
+                    const void* k_norm_w, const void* k_norm_b, float eps,
+                    const int32_t* positions, int rope_dims, int32_t sec_t,
+                    int32_t sec_h, int32_t sec_w, float rope_theta,
+                    int rope_style, float q_scale, void* q_out, void* k_out,
+                    void* v_out, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                    int dtype, void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fr_status_string(int status);

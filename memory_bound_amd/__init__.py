@@ -26,6 +26,8 @@ W_NONE, W_MUL, W_ONE_PLUS = 0, 1, 2
 Q_STATIC, Q_TOKEN = 0, 1
 ACT_SWIGLU, ACT_GEGLU_TANH, ACT_SQRELU = 0, 1, 2
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
+NORM_NONE, NORM_RMS, NORM_LAYER = 0, 1, 2
+SCOPE_HEAD, SCOPE_FULL = 0, 1
 
 FR_OK, FR_ERR_NULL, FR_ERR_SHAPE, FR_ERR_DTYPE, FR_ERR_ALIGN, FR_ERR_MODE, \
     FR_ERR_UNSUPPORTED, FR_ERR_LAUNCH = range(8)
@@ -58,6 +60,9 @@ _SIGS = {
     "fr_resid_rmsnorm_mxfp4": [_P, _P, _P, _P, _INT, _F, _P, _P, _I64, _I64,
                                _INT, _P],
     "fr_gated_act_mxfp4": [_P, _INT, _P, _P, _I64, _I64, _INT, _P],
+    "fr_qk_norm_rope": [_P, _INT, _INT, _P, _P, _P, _P, _F, _P, _INT, _I32,
+                        _I32, _I32, _F, _INT, _F, _P, _P, _P, _I64, _I32, _I32,
+                        _I32, _INT, _P],
     "fr_decode_chain_persistent": [_P, _P, _P, _P, _P, _P, _F, _F, _P, _P, _F,
                                    _INT, _P, _P, _P, _P, _I32, _I32, _I32, _P,
                                    _I32, _I32, _I64, _I64, _I32, _I32, _I32,
@@ -192,6 +197,18 @@ def fr_decode_chain_persistent(x, gate, ada_scale, ada_shift, residual,
         rope_theta, rope_style, _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
         _ptr(page_table), page_table_len, page_size, num_pages, _ptr(err_flag),
         layers, steps, T, H, Hq, Hkv, D, dtype, _stream(stream)))
+
+
+def fr_qk_norm_rope(qkv, norm_kind, norm_scope, q_norm_w, q_norm_b, k_norm_w,
+                    k_norm_b, eps, positions, rope_dims, sections, rope_theta,
+                    rope_style, q_scale, q_out, k_out, v_out, T, Hq, Hkv, D,
+                    dtype, stream=None):
+    sec = tuple(sections) if sections is not None else (0, 0, 0)
+    _check(lib.fr_qk_norm_rope(
+        _ptr(qkv), norm_kind, norm_scope, _ptr(q_norm_w), _ptr(q_norm_b),
+        _ptr(k_norm_w), _ptr(k_norm_b), eps, _ptr(positions), rope_dims, *sec,
+        rope_theta, rope_style, q_scale, _ptr(q_out), _ptr(k_out), _ptr(v_out),
+        T, Hq, Hkv, D, dtype, _stream(stream)))
 
 
 def fr_gemm_gated_act_fp8(a, a_scales, w_packed, w_scales, act, out_fp8,

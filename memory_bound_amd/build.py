@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfrhip.so")
 SOURCES = ["fr_api.hip", "fr_norm.hip", "fr_qkv.hip", "fr_act.hip", "fr_gemm.hip",
-           "fr_chain.hip"]
+           "fr_chain.hip", "fr_qknorm.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -340,6 +340,66 @@ FR_EXPORT int fr_decode_chain_persistent(
     return launch_status(fr::launch_chain(a, dtype, (hipStream_t)stream));
 }
 
+FR_EXPORT int fr_qk_norm_rope(const void* qkv, int norm_kind, int norm_scope,
+                              const void* q_norm_w, const void* q_norm_b,
+                              const void* k_norm_w, const void* k_norm_b, float eps,
+                              const int32_t* positions, int rope_dims,
+                              int32_t sec_t, int32_t sec_h, int32_t sec_w,
+                              float rope_theta, int rope_style, float q_scale,
+                              void* q_out, void* k_out, void* v_out, int64_t T,
+                              int32_t Hq, int32_t Hkv, int32_t D, int dtype,
+                              void* stream) {
+    if (dtype != FR_F16 && dtype != FR_BF16) return FR_ERR_DTYPE;
+    if (T < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || D % 16 != 0) return FR_ERR_SHAPE;
+    if (D > 256 || T > 0x7fffffffLL) return FR_ERR_UNSUPPORTED;
+    int lp = 1;
+    while (lp < D / 16) lp *= 2;
+    if (((int64_t)Hq + 2 * (int64_t)Hkv) * lp > 1024) return FR_ERR_UNSUPPORTED;
+    if (norm_kind != FR_NORM_NONE && norm_kind != FR_NORM_RMS && norm_kind != FR_NORM_LAYER)
+        return FR_ERR_MODE;
+    if (norm_scope != FR_SCOPE_HEAD && norm_scope != FR_SCOPE_FULL) return FR_ERR_MODE;
+    if (rope_dims != 1 && rope_dims != 3) return FR_ERR_MODE;
+    if (rope_dims == 3 && (sec_t < 1 || sec_h < 1 || sec_w < 1 || sec_t + sec_h + sec_w != D / 2))
+        return FR_ERR_SHAPE;
+    if (rope_style != FR_ROPE_HALF && rope_style != FR_ROPE_INTERLEAVED) return FR_ERR_MODE;
+    if (!finite_nonneg(eps)) return FR_ERR_MODE;
+    if (!(isfinite(rope_theta) && rope_theta > 1.0f)) return FR_ERR_MODE;
+    if (!(isfinite(q_scale) && q_scale > 0.0f)) return FR_ERR_MODE;
+    if (!qkv || !positions || !q_out || !k_out || !v_out) return FR_ERR_NULL;
+    if (!aligned16(qkv) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(v_out))
+        return FR_ERR_ALIGN;
+    const void* ws[4] = {q_norm_w, q_norm_b, k_norm_w, k_norm_b};
+    for (const void* w : ws)
+        if (w && !aligned16(w)) return FR_ERR_ALIGN;
+    if (!aligned4(positions)) return FR_ERR_ALIGN;
+    if (T == 0) return FR_OK;
+    fr::QkNormArgs a{};
+    a.qkv = qkv;
+    a.qw = q_norm_w;
+    a.qb = q_norm_b;
+    a.kw = k_norm_w;
+    a.kb = k_norm_b;
+    a.pos = positions;
+    a.q_out = q_out;
+    a.k_out = k_out;
+    a.v_out = v_out;
+    a.T = T;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.norm_kind = norm_kind;
+    a.full = norm_scope == FR_SCOPE_FULL;
+    a.rope3 = rope_dims == 3;
+    a.sec[0] = sec_t;
+    a.sec[1] = sec_h;
+    a.sec[2] = sec_w;
+    a.style = rope_style;
+    a.eps = eps;
+    a.theta = rope_theta;
+    a.q_scale = q_scale;
+    return launch_status(fr::launch_qknr(a, dtype, (hipStream_t)stream));
+}
+
 FR_EXPORT const char* fr_status_string(int status) {
     switch (status) {
     case FR_OK: return "FR_OK";

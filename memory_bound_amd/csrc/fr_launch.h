@@ -116,6 +116,29 @@ struct ChainArgs {
 };
 hipError_t launch_chain(const ChainArgs& a, int dtype, hipStream_t s);
 
+// Packed QKV split + Q/K norm (RMS / Layer, per head / full width) + RoPE
+// (1D / 3D) into separate Q, K, V outputs.
+struct QkNormArgs {
+    const void* qkv;        // [T, (Hq + 2 Hkv) D]
+    const void* qw;         // [D] or [Hq D]
+    const void* qb;
+    const void* kw;         // [D] or [Hkv D]
+    const void* kb;
+    const int32_t* pos;     // [T] or [T, 3]
+    void* q_out;            // [T, Hq, D]
+    void* k_out;            // [T, Hkv, D]
+    void* v_out;            // [T, Hkv, D]
+    int64_t T;
+    int Hq, Hkv, D;
+    int norm_kind;          // 0 none, 1 RMS, 2 Layer
+    int full;               // norm over the full Q (K) width
+    int rope3;              // 3D RoPE
+    int sec[3];             // 3D RoPE pairs per axis
+    int style;
+    float eps, theta, q_scale;
+};
+hipError_t launch_qknr(const QkNormArgs& a, int dtype, hipStream_t s);
+
 enum { NORM_FP8 = 0, NORM_ADA_FP8 = 1, NORM_MXFP4 = 2 };
 hipError_t launch_norm(const NormArgs& a, int dtype, int kind, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int dtype, hipStream_t s);

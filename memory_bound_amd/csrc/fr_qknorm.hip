@@ -1,0 +1,279 @@
+// fr_qknorm.hip -- packed QKV split + Q/K norm + RoPE, the variants of the
+// Q/K post-processing contract, one kernel.
+//
+// Definitions: "FlashRT cross-layer fusion" article, section 2.2 (one
+// kernel normalises Q and K and rotates them, V passes through; the
+// Chameleon prefill path uses LayerNorm per head with rotate-half RoPE and
+// keeps each RoPE pair in one lane; the Wan video path splits the packed
+// row three ways, RMS-normalises Q and K over their full width and applies a
+// 3D RoPE, in one streaming read).
+//
+// Mapping: one workgroup (4 waves) per token.  LP lanes (a power of two >=
+// D/16) serve one head; lane j of a head holds the 16-byte chunk j of the
+// first half of the head and chunk j of the second half, so every RoPE
+// pair -- rotate-half (i, i + D/2) or interleaved (2i, 2i+1) -- sits in one
+// lane.  The token's heads are covered in U passes of 256/LP heads, all
+// loaded before any arithmetic and kept in registers, so a full-width norm
+// needs no second read: its sums are a wave reduction plus one LDS step
+// (fp64, so they do not depend on the order).  A per-head norm is a DPP
+// reduction over the head's lanes.  LayerNorm subtracts the mean first
+// (two reductions).  Each lane's 8 rotation angles depend only on its lane
+// and the token, so they are computed once (fp64, as in op b) and serve
+// every head of the lane; 3D RoPE splits the pairs into time / height /
+// width ranges, each turned by its own position.
+#include "fr_device.h"
+#include "fr_launch.h"
+
+namespace fr {
+
+template <int DT, int LP, int U>
+__global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
+    __shared__ double red[4][4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int64_t t = blockIdx.x;
+    constexpr int HPB = 256 / LP;                        // heads per pass
+    const int D = a.D, L16 = D >> 4;
+    const int NH = a.Hq + 2 * a.Hkv;
+    const int j = tid & (LP - 1);
+    const int off0 = j * 16, off1 = D + j * 16;          // byte offsets in a head
+    const bool lane_ok = j < L16;
+
+    // ---- loads: every head of the token, U passes ----
+    const char* rowp = (const char*)a.qkv + t * (int64_t)NH * D * 2;
+    u32x4 c0[U], c1[U];
+    int head[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        head[u] = u * HPB + tid / LP;
+        c0[u] = c1[u] = (u32x4){0, 0, 0, 0};
+        if (lane_ok && head[u] < NH) {
+            const char* src = rowp + (int64_t)head[u] * D * 2;
+            c0[u] = ld128_stream(src + off0);
+            c1[u] = ld128_stream(src + off1);
+        }
+    }
+    float v[U][16];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[u][2 * e] = lo16<DT>(c0[u][e]);
+            v[u][2 * e + 1] = hi16<DT>(c0[u][e]);
+            v[u][8 + 2 * e] = lo16<DT>(c1[u][e]);
+            v[u][8 + 2 * e + 1] = hi16<DT>(c1[u][e]);
+        }
+    auto part = [&](int h) { return h < a.Hq ? 0 : (h < a.Hq + a.Hkv ? 1 : 2); };  // Q, K, V
+
+    // ---- norm statistics (per unit: mean[u], rstd[u]) ----
+    float mean[U], rstd[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { mean[u] = 0.0f; rstd[u] = 1.0f; }
+    if (a.norm_kind != 0) {
+        const bool layer = a.norm_kind == 2;
+        if (a.full) {
+            // sums over all Q values and over all K values of the token
+            double sq = 0.0, sk = 0.0;
+            double mq = 0.0, mk = 0.0;
+            if (layer) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    double s = 0.0;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) s += (double)v[u][e];
+                    const int p = part(head[u]);
+                    if (p == 0) sq += s; else if (p == 1) sk += s;
+                }
+                sq = wave_sum_d(sq);
+                sk = wave_sum_d(sk);
+                if (lane == 0) { red[wv][0] = sq; red[wv][1] = sk; }
+                __syncthreads();
+                mq = (red[0][0] + red[1][0] + red[2][0] + red[3][0]) / ((double)a.Hq * D);
+                mk = (red[0][1] + red[1][1] + red[2][1] + red[3][1]) / ((double)a.Hkv * D);
+                sq = sk = 0.0;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = part(head[u]);
+                const double m = p == 0 ? mq : mk;
+                double s = 0.0;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const double d = (double)v[u][e] - m;
+                    s = fma(d, d, s);
+                }
+                if (!lane_ok) s = 0.0;
+                if (p == 0) sq += s; else if (p == 1) sk += s;
+            }
+            sq = wave_sum_d(sq);
+            sk = wave_sum_d(sk);
+            if (lane == 0) { red[wv][2] = sq; red[wv][3] = sk; }
+            __syncthreads();
+            const double vq = (red[0][2] + red[1][2] + red[2][2] + red[3][2]) / ((double)a.Hq * D);
+            const double vk = (red[0][3] + red[1][3] + red[2][3] + red[3][3]) / ((double)a.Hkv * D);
+            const float rq = (float)(1.0 / sqrt(vq + (double)a.eps));
+            const float rk = (float)(1.0 / sqrt(vk + (double)a.eps));
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = part(head[u]);
+                mean[u] = (float)(p == 0 ? mq : mk);
+                rstd[u] = p == 0 ? rq : rk;
+            }
+        } else {
+            // per head, over the head's LP lanes
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float m = 0.0f;
+                if (layer) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) s += v[u][e];
+                    m = group_reduce<LP>(s, OpSum()) / (float)D;
+                }
+                float ss = 0.0f;
+                if (lane_ok) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float d = v[u][e] - m;
+                        ss = fmaf(d, d, ss);
+                    }
+                }
+                ss = group_reduce<LP>(ss, OpSum());
+                mean[u] = m;
+                rstd[u] = 1.0f / sqrtf(ss / (float)D + a.eps);
+            }
+        }
+    }
+
+    // ---- this lane's 8 rotation angles ----
+    float cs[8], sn[8];
+    {
+        const double l2t = log2((double)a.theta);
+        const int* pp = a.pos + (a.rope3 ? 3 * t : t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = a.style == 0 ? 8 * j + e : (e < 4 ? 4 * j + e : (D >> 2) + 4 * j + (e - 4));
+            double ang;
+            if (a.rope3) {
+                const int ax = i < a.sec[0] ? 0 : (i < a.sec[0] + a.sec[1] ? 1 : 2);
+                const int k = i - (ax > 0 ? a.sec[0] : 0) - (ax > 1 ? a.sec[1] : 0);
+                ang = (double)pp[ax] * exp2(-(double)k / (double)a.sec[ax] * l2t);
+            } else {
+                ang = (double)pp[0] * exp2(-(double)(2 * i) / (double)D * l2t);
+            }
+            sincos_pos(ang, &sn[e], &cs[e]);
+        }
+    }
+
+    // per-head norm weights are the same for every head of the lane
+    u32x4 hw0[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, hw1[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    u32x4 hb0[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, hb1[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    if (a.norm_kind != 0 && !a.full && lane_ok) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const void* w = p == 0 ? a.qw : a.kw;
+            const void* b = p == 0 ? a.qb : a.kb;
+            if (w) { hw0[p] = ld128((const char*)w + off0); hw1[p] = ld128((const char*)w + off1); }
+            if (b) { hb0[p] = ld128((const char*)b + off0); hb1[p] = ld128((const char*)b + off1); }
+        }
+    }
+
+    // ---- apply, rotate, store ----
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int h = head[u];
+        if (!lane_ok || h >= NH) continue;
+        const int p = part(h);
+        char* dst;
+        if (p == 2) {                                    // V: bit copy
+            dst = (char*)a.v_out + (t * a.Hkv + (h - a.Hq - a.Hkv)) * (int64_t)D * 2;
+            st128_stream(dst + off0, c0[u]);
+            st128_stream(dst + off1, c1[u]);
+            continue;
+        }
+        const int hl = p == 0 ? h : h - a.Hq;            // head within Q or K
+        if (a.norm_kind != 0) {
+            u32x4 w0 = hw0[p], w1 = hw1[p], b0 = hb0[p], b1 = hb1[p];
+            const void* w = p == 0 ? a.qw : a.kw;
+            const void* b = p == 0 ? a.qb : a.kb;
+            if (a.full) {                                // weights of this head's slice
+                const int64_t o = (int64_t)hl * D * 2;
+                if (w) { w0 = ld128((const char*)w + o + off0); w1 = ld128((const char*)w + o + off1); }
+                if (b) { b0 = ld128((const char*)b + o + off0); b1 = ld128((const char*)b + o + off1); }
+            }
+            const bool layer = a.norm_kind == 2;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const u32 ww = e < 4 ? w0[e] : w1[e - 4];
+                const u32 bb = e < 4 ? b0[e] : b1[e - 4];
+                const int ia = e < 4 ? 2 * e : 8 + 2 * (e - 4);
+                const float wa = w ? lo16<DT>(ww) : 1.0f, wb = w ? hi16<DT>(ww) : 1.0f;
+                const float ba = (layer && b) ? lo16<DT>(bb) : 0.0f;
+                const float bbv = (layer && b) ? hi16<DT>(bb) : 0.0f;
+                v[u][ia] = fmaf((v[u][ia] - mean[u]) * rstd[u], wa, ba);
+                v[u][ia + 1] = fmaf((v[u][ia + 1] - mean[u]) * rstd[u], wb, bbv);
+            }
+        }
+        if (a.style == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x0 = v[u][e], x1 = v[u][8 + e];
+                v[u][e] = fmaf(x0, cs[e], -x1 * sn[e]);
+                v[u][8 + e] = fmaf(x1, cs[e], x0 * sn[e]);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int b = m < 4 ? 2 * m : 8 + 2 * (m - 4);
+                const float x0 = v[u][b], x1 = v[u][b + 1];
+                v[u][b] = fmaf(x0, cs[m], -x1 * sn[m]);
+                v[u][b + 1] = fmaf(x1, cs[m], x0 * sn[m]);
+            }
+        }
+        const float qs = p == 0 ? a.q_scale : 1.0f;
+        u32x4 o0, o1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o0[e] = pack16<DT>(v[u][2 * e] * qs, v[u][2 * e + 1] * qs);
+            o1[e] = pack16<DT>(v[u][8 + 2 * e] * qs, v[u][8 + 2 * e + 1] * qs);
+        }
+        dst = p == 0 ? (char*)a.q_out + (t * a.Hq + hl) * (int64_t)D * 2
+                     : (char*)a.k_out + (t * a.Hkv + hl) * (int64_t)D * 2;
+        st128_stream(dst + off0, o0);
+        st128_stream(dst + off1, o1);
+    }
+}
+
+template <int DT, int LP>
+static hipError_t launch_qknr_lp(const QkNormArgs& a, int u, hipStream_t s) {
+    const void* fn = u == 1 ? (const void*)k_qknr<DT, LP, 1>
+                   : u == 2 ? (const void*)k_qknr<DT, LP, 2> : (const void*)k_qknr<DT, LP, 4>;
+    QkNormArgs copy = a;
+    void* args[] = {&copy};
+    return hipLaunchKernel(fn, dim3((unsigned)a.T), dim3(256), args, 0, s);
+}
+
+template <int DT>
+static hipError_t launch_qknr_dt(const QkNormArgs& a, int lp, int u, hipStream_t s) {
+    switch (lp) {
+    case 1: return launch_qknr_lp<DT, 1>(a, u, s);
+    case 2: return launch_qknr_lp<DT, 2>(a, u, s);
+    case 4: return launch_qknr_lp<DT, 4>(a, u, s);
+    case 8: return launch_qknr_lp<DT, 8>(a, u, s);
+    default: return launch_qknr_lp<DT, 16>(a, u, s);
+    }
+}
+
+// U: passes of 256/LP heads; the caller guarantees NH * LP <= 4 * 256.
+hipError_t launch_qknr(const QkNormArgs& a, int dtype, hipStream_t s) {
+    int lp = 1;
+    while (lp < a.D / 16) lp *= 2;
+    const int NH = a.Hq + 2 * a.Hkv;
+    const int passes = (NH * lp + 255) / 256;
+    const int u = passes <= 1 ? 1 : (passes <= 2 ? 2 : 4);
+    return dtype == DT_BF16 ? launch_qknr_dt<DT_BF16>(a, lp, u, s)
+                            : launch_qknr_dt<DT_F16>(a, lp, u, s);
+}
+
+}  // namespace fr

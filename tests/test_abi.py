@@ -29,7 +29,8 @@ def test_header_declares_the_four_ops_and_helpers():
         "fr_resid_rmsnorm_fp8", "fr_adarms_gate_res_fp8",
         "fr_qkv_normrope_kvwrite", "fr_gated_act_fp8", "fr_gemm_gated_act_fp8",
         "fr_gemm_pack_weights", "fr_resid_rmsnorm_mxfp4", "fr_gated_act_mxfp4",
-        "fr_decode_chain_persistent", "fr_status_string", "fr_abi_version"])
+        "fr_decode_chain_persistent", "fr_qk_norm_rope", "fr_status_string",
+        "fr_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -264,3 +265,41 @@ def chain(**kw):
 ])
 def test_decode_chain_persistent_validation(kw, status):
     assert chain(**kw) == status
+
+
+def qknr(**kw):
+    args = dict(qkv=A, norm_kind=1, norm_scope=0, q_norm_w=None, q_norm_b=None,
+                k_norm_w=None, k_norm_b=None, eps=1e-6, positions=B, rope_dims=1,
+                sec_t=0, sec_h=0, sec_w=0, rope_theta=1e4, rope_style=0, q_scale=1.0,
+                q_out=C, k_out=D_, v_out=E, T=10, Hq=8, Hkv=2, D=128, dtype=fr.BF16)
+    args.update(kw)
+    order = ["qkv", "norm_kind", "norm_scope", "q_norm_w", "q_norm_b", "k_norm_w",
+             "k_norm_b", "eps", "positions", "rope_dims", "sec_t", "sec_h", "sec_w",
+             "rope_theta", "rope_style", "q_scale", "q_out", "k_out", "v_out", "T",
+             "Hq", "Hkv", "D", "dtype"]
+    return fr.lib.fr_qk_norm_rope(*[args[k] for k in order], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkv=None), fr.FR_ERR_NULL),
+    (dict(v_out=None), fr.FR_ERR_NULL),
+    (dict(norm_kind=3), fr.FR_ERR_MODE),
+    (dict(norm_scope=2), fr.FR_ERR_MODE),
+    (dict(rope_dims=2), fr.FR_ERR_MODE),
+    (dict(rope_dims=3, sec_t=20, sec_h=20, sec_w=20), fr.FR_ERR_SHAPE),
+    (dict(rope_dims=3, sec_t=64, sec_h=0, sec_w=0), fr.FR_ERR_SHAPE),
+    (dict(rope_dims=3, sec_t=22, sec_h=21, sec_w=21), fr.FR_OK),
+    (dict(D=100), fr.FR_ERR_SHAPE),
+    (dict(D=512), fr.FR_ERR_UNSUPPORTED),
+    (dict(Hq=300, Hkv=20), fr.FR_ERR_UNSUPPORTED),
+    (dict(q_scale=0.0), fr.FR_ERR_MODE),
+    (dict(q_norm_w=F + 4), fr.FR_ERR_ALIGN),
+    (dict(positions=B + 2), fr.FR_ERR_ALIGN),
+    (dict(dtype=4), fr.FR_ERR_DTYPE),
+    (dict(T=0), fr.FR_OK),
+])
+def test_qk_norm_rope_validation(kw, status):
+    kw = dict(kw)
+    if kw.get("rope_dims") == 3 and kw.get("sec_t") == 22:
+        kw["T"] = 0                       # valid sections; launch nothing
+    assert qknr(**kw) == status

@@ -187,3 +187,31 @@ def gemm_inputs(M, K, I, seed, scale_lo=0.5, scale_hi=2.0):
     a_s = rng.uniform(scale_lo, scale_hi, (M, K // 128)).astype(np.float32) * unit
     w_s = rng.uniform(scale_lo, scale_hi, (2 * I // 128, K // 128)).astype(np.float32) * np.float32(1.0 / 32.0)
     return {"a": a, "a_scales": a_s, "w": w, "w_scales": w_s}
+
+
+# ---------------------------------------------------------------------------
+# Q/K norm + RoPE variants (Chameleon LayerNorm per head, Wan full-width
+# RMSNorm + 3D RoPE)
+# ---------------------------------------------------------------------------
+
+def qk_norm_rope_inputs(T, Hq, Hkv, D, dtype, seed, scope_full=False, rope3=False,
+                        grid=(4, 8, 8), norm_std=0.05):
+    """qkv ~ N(0,1) [T, (Hq+2Hkv)D]; norm weights 1 + N(0, norm_std^2) and
+    biases N(0, norm_std^2), [D] per head or [Hq D] / [Hkv D] full width;
+    positions 0..T-1, or for 3D the (time, height, width) coordinates of
+    token t on a frames x height x width grid in raster order."""
+    rng = np.random.default_rng(seed)
+    qkv = normal(rng, (T, (Hq + 2 * Hkv) * D))
+    nq, nk = (Hq * D, Hkv * D) if scope_full else (D, D)
+    out = {"qkv": to16(qkv, dtype),
+           "q_norm_w": to16(normal(rng, (nq,), std=norm_std, mean=1.0), dtype),
+           "q_norm_b": to16(normal(rng, (nq,), std=norm_std), dtype),
+           "k_norm_w": to16(normal(rng, (nk,), std=norm_std, mean=1.0), dtype),
+           "k_norm_b": to16(normal(rng, (nk,), std=norm_std), dtype)}
+    if rope3:
+        f, h, w = grid
+        t = np.arange(T)
+        out["positions"] = np.stack([t // (h * w), (t // w) % h, t % w], axis=1).astype(np.int32)
+    else:
+        out["positions"] = np.arange(T, dtype=np.int32)
+    return out
