@@ -193,6 +193,7 @@ def main():
                     f(i)
         torch.cuda.synchronize()
         run_mxfp4(torch, fr, workloads, dev, stream, 3, timed=False)
+        run_qknorm(torch, fr, workloads, dev, stream, 3, timed=False)
         run_gemm_act(torch, fr, workloads, dev, stream, reps=3, timed=False,
                      shapes=((128, 2048, 6144),))
         print(json.dumps({"pmc_pass": True, "copy_bytes_each_way": 1 << 30,
@@ -286,6 +287,9 @@ def main():
     # ---- MX FP4 producers at 8192 tokens ---------------------------------
     mxfp4 = run_mxfp4(torch, fr, workloads, dev, stream, args.steps)
 
+    # ---- Q/K norm + RoPE variants at 8192 tokens -------------------------
+    qknorm = run_qknorm(torch, fr, workloads, dev, stream, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
@@ -319,6 +323,7 @@ def main():
         "decode_t10": small,
         "gemm_gated_act_fp8": gemm,
         "mxfp4_producers": mxfp4,
+        "qk_norm_rope_variants": qknorm,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
@@ -528,6 +533,58 @@ def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
         out[name] = {"bytes": nb, "us_per_launch": round(us, 3),
                      "GBps": round(nb / (us * 1e-6) / 1e9, 1),
                      "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def run_qknorm(torch, fr, workloads, dev, stream, reps, timed=True):
+    """fr_qk_norm_rope at 8192 tokens: the Wan-style full-width RMSNorm + 3D
+    RoPE (40/40 heads x 128 bf16) and the Chameleon-style LayerNorm per head
+    + RoPE (32/32 heads x 128 bf16); buffers rotated through >= 512 MB."""
+    T, D = T_BIG, 128
+    out = {}
+    for name, Hq, Hkv, kind, full, r3, sec, style in (
+            ("wan_rms_full_3d_T8192_40x128", 40, 40, fr.NORM_RMS, True, True, (22, 21, 21), 1),
+            ("chameleon_layer_head_T8192_32x128", 32, 32, fr.NORM_LAYER, False, False, None, 0)):
+        NH = Hq + 2 * Hkv
+        nb = 2 * T * NH * D * 2 + 4 * T * (3 if r3 else 1)
+        inp = workloads.qk_norm_rope_inputs(T, Hq, Hkv, D, workloads.BF16, 610,
+                                            scope_full=full, rope3=r3, grid=(8, 32, 32))
+        w = {k: dev(inp[k]) for k in ("q_norm_w", "q_norm_b", "k_norm_w", "k_norm_b", "positions")}
+        sets = []
+        for _ in range(max(2, -(-(512 << 20) // nb)) if timed else 1):
+            sets.append({"qkv": dev(inp["qkv"]),
+                         "q": torch.empty((T, Hq, D), dtype=torch.int16, device="cuda"),
+                         "k": torch.empty((T, Hkv, D), dtype=torch.int16, device="cuda"),
+                         "v": torch.empty((T, Hkv, D), dtype=torch.int16, device="cuda")})
+
+        def f(i):
+            d = sets[i % len(sets)]
+            fr.fr_qk_norm_rope(d["qkv"], kind, int(full), w["q_norm_w"], w["q_norm_b"],
+                               w["k_norm_w"], w["k_norm_b"], EPS, w["positions"],
+                               3 if r3 else 1, sec, 1e4, style, 1.0, d["q"], d["k"],
+                               d["v"], T, Hq, Hkv, D, fr.BF16, stream=stream)
+        for i in range(3):
+            f(i)
+        torch.cuda.synchronize()
+        if not timed:
+            continue
+        runs = []
+        with torch.cuda.stream(stream):                  # spin on the same stream
+            for _ in range(GROUP_REPEATS):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(SPIN_CYCLES)
+                e0.record(stream)
+                for i in range(reps):
+                    f(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                runs.append(e0.elapsed_time(e1) * 1e3 / reps)
+        us = float(np.median(runs))
+        out[name] = {"bytes": nb, "us_per_launch": round(us, 3),
+                     "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del sets
     return out
 
 

@@ -17,10 +17,12 @@
 // needs no second read: its sums are a wave reduction plus one LDS step
 // (fp64, so they do not depend on the order).  A per-head norm is a DPP
 // reduction over the head's lanes.  LayerNorm subtracts the mean first
-// (two reductions).  Each lane's 8 rotation angles depend only on its lane
-// and the token, so they are computed once (fp64, as in op b) and serve
-// every head of the lane; 3D RoPE splits the pairs into time / height /
-// width ranges, each turned by its own position.
+// (two reductions).  The token's D/2 rotation angles are computed once per
+// workgroup (one per thread, fp64 as in op b) into LDS and serve every
+// head; 3D RoPE splits the pairs into time / height / width ranges, each
+// turned by its own position.  Heads stay in registers as raw 16-bit pairs
+// and are widened on use (one shift or convert each), which keeps four
+// passes of heads within 128 registers.
 #include "fr_device.h"
 #include "fr_launch.h"
 
@@ -29,6 +31,7 @@ namespace fr {
 template <int DT, int LP, int U>
 __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
     __shared__ double red[4][4];
+    __shared__ float tab[2][128];                        // cos / sin of the token
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
@@ -54,16 +57,26 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
             c1[u] = ld128_stream(src + off1);
         }
     }
-    float v[U][16];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[u][2 * e] = lo16<DT>(c0[u][e]);
-            v[u][2 * e + 1] = hi16<DT>(c0[u][e]);
-            v[u][8 + 2 * e] = lo16<DT>(c1[u][e]);
-            v[u][8 + 2 * e + 1] = hi16<DT>(c1[u][e]);
+    // the token's D/2 angles, one per thread, while the loads are in flight
+    if (tid < (D >> 1)) {
+        const double l2t = log2((double)a.theta);
+        const int* pp = a.pos + (a.rope3 ? 3 * t : t);
+        double ang;
+        if (a.rope3) {
+            const int i = tid;
+            const int ax = i < a.sec[0] ? 0 : (i < a.sec[0] + a.sec[1] ? 1 : 2);
+            const int k = i - (ax > 0 ? a.sec[0] : 0) - (ax > 1 ? a.sec[1] : 0);
+            ang = (double)pp[ax] * exp2(-(double)k / (double)a.sec[ax] * l2t);
+        } else {
+            ang = (double)pp[0] * exp2(-(double)(2 * tid) / (double)D * l2t);
         }
+        sincos_pos(ang, &tab[1][tid], &tab[0][tid]);
+    }
+    // value e of unit u (0..7: chunk j of the first half, 8..15: second half)
+    auto val = [&](int u, int e) -> float {
+        const u32 w = e < 8 ? c0[u][(e & 7) >> 1] : c1[u][(e & 7) >> 1];
+        return (e & 1) ? hi16<DT>(w) : lo16<DT>(w);
+    };
     auto part = [&](int h) { return h < a.Hq ? 0 : (h < a.Hq + a.Hkv ? 1 : 2); };  // Q, K, V
 
     // ---- norm statistics (per unit: mean[u], rstd[u]) ----
@@ -81,7 +94,7 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
                 for (int u = 0; u < U; ++u) {
                     double s = 0.0;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) s += (double)v[u][e];
+                    for (int e = 0; e < 16; ++e) s += (double)val(u, e);
                     const int p = part(head[u]);
                     if (p == 0) sq += s; else if (p == 1) sk += s;
                 }
@@ -100,7 +113,7 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
                 double s = 0.0;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const double d = (double)v[u][e] - m;
+                    const double d = (double)val(u, e) - m;
                     s = fma(d, d, s);
                 }
                 if (!lane_ok) s = 0.0;
@@ -128,14 +141,14 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
                 if (layer) {
                     float s = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) s += v[u][e];
+                    for (int e = 0; e < 16; ++e) s += val(u, e);
                     m = group_reduce<LP>(s, OpSum()) / (float)D;
                 }
                 float ss = 0.0f;
                 if (lane_ok) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        const float d = v[u][e] - m;
+                        const float d = val(u, e) - m;
                         ss = fmaf(d, d, ss);
                     }
                 }
@@ -146,38 +159,7 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
         }
     }
 
-    // ---- this lane's 8 rotation angles ----
-    float cs[8], sn[8];
-    {
-        const double l2t = log2((double)a.theta);
-        const int* pp = a.pos + (a.rope3 ? 3 * t : t);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int i = a.style == 0 ? 8 * j + e : (e < 4 ? 4 * j + e : (D >> 2) + 4 * j + (e - 4));
-            double ang;
-            if (a.rope3) {
-                const int ax = i < a.sec[0] ? 0 : (i < a.sec[0] + a.sec[1] ? 1 : 2);
-                const int k = i - (ax > 0 ? a.sec[0] : 0) - (ax > 1 ? a.sec[1] : 0);
-                ang = (double)pp[ax] * exp2(-(double)k / (double)a.sec[ax] * l2t);
-            } else {
-                ang = (double)pp[0] * exp2(-(double)(2 * i) / (double)D * l2t);
-            }
-            sincos_pos(ang, &sn[e], &cs[e]);
-        }
-    }
-
-    // per-head norm weights are the same for every head of the lane
-    u32x4 hw0[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, hw1[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-    u32x4 hb0[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, hb1[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-    if (a.norm_kind != 0 && !a.full && lane_ok) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const void* w = p == 0 ? a.qw : a.kw;
-            const void* b = p == 0 ? a.qb : a.kb;
-            if (w) { hw0[p] = ld128((const char*)w + off0); hw1[p] = ld128((const char*)w + off1); }
-            if (b) { hb0[p] = ld128((const char*)b + off0); hb1[p] = ld128((const char*)b + off1); }
-        }
-    }
+    __syncthreads();                                     // angle table complete
 
     // ---- apply, rotate, store ----
 #pragma unroll
@@ -193,15 +175,18 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
             continue;
         }
         const int hl = p == 0 ? h : h - a.Hq;            // head within Q or K
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = val(u, e);
         if (a.norm_kind != 0) {
-            u32x4 w0 = hw0[p], w1 = hw1[p], b0 = hb0[p], b1 = hb1[p];
+            // weights [D] shared by the heads, or this head's slice of the
+            // full-width weights (cache-resident either way)
             const void* w = p == 0 ? a.qw : a.kw;
             const void* b = p == 0 ? a.qb : a.kb;
-            if (a.full) {                                // weights of this head's slice
-                const int64_t o = (int64_t)hl * D * 2;
-                if (w) { w0 = ld128((const char*)w + o + off0); w1 = ld128((const char*)w + o + off1); }
-                if (b) { b0 = ld128((const char*)b + o + off0); b1 = ld128((const char*)b + o + off1); }
-            }
+            const int64_t o = a.full ? (int64_t)hl * D * 2 : 0;
+            u32x4 w0 = {0, 0, 0, 0}, w1 = w0, b0 = w0, b1 = w0;
+            if (w) { w0 = ld128((const char*)w + o + off0); w1 = ld128((const char*)w + o + off1); }
+            if (b) { b0 = ld128((const char*)b + o + off0); b1 = ld128((const char*)b + o + off1); }
             const bool layer = a.norm_kind == 2;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -211,32 +196,37 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
                 const float wa = w ? lo16<DT>(ww) : 1.0f, wb = w ? hi16<DT>(ww) : 1.0f;
                 const float ba = (layer && b) ? lo16<DT>(bb) : 0.0f;
                 const float bbv = (layer && b) ? hi16<DT>(bb) : 0.0f;
-                v[u][ia] = fmaf((v[u][ia] - mean[u]) * rstd[u], wa, ba);
-                v[u][ia + 1] = fmaf((v[u][ia + 1] - mean[u]) * rstd[u], wb, bbv);
+                v[ia] = fmaf((v[ia] - mean[u]) * rstd[u], wa, ba);
+                v[ia + 1] = fmaf((v[ia + 1] - mean[u]) * rstd[u], wb, bbv);
             }
         }
+        // rotate-half: pair e = (8j+e, D/2+8j+e); interleaved: pair m of
+        // chunk 0 = angle 4j+m, of chunk 1 = angle D/4+4j+m
         if (a.style == 0) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x0 = v[u][e], x1 = v[u][8 + e];
-                v[u][e] = fmaf(x0, cs[e], -x1 * sn[e]);
-                v[u][8 + e] = fmaf(x1, cs[e], x0 * sn[e]);
+                const float cs = tab[0][8 * j + e], sn = tab[1][8 * j + e];
+                const float x0 = v[e], x1 = v[8 + e];
+                v[e] = fmaf(x0, cs, -x1 * sn);
+                v[8 + e] = fmaf(x1, cs, x0 * sn);
             }
         } else {
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
+                const int i = m < 4 ? 4 * j + m : (D >> 2) + 4 * j + (m - 4);
                 const int b = m < 4 ? 2 * m : 8 + 2 * (m - 4);
-                const float x0 = v[u][b], x1 = v[u][b + 1];
-                v[u][b] = fmaf(x0, cs[m], -x1 * sn[m]);
-                v[u][b + 1] = fmaf(x1, cs[m], x0 * sn[m]);
+                const float cs = tab[0][i], sn = tab[1][i];
+                const float x0 = v[b], x1 = v[b + 1];
+                v[b] = fmaf(x0, cs, -x1 * sn);
+                v[b + 1] = fmaf(x1, cs, x0 * sn);
             }
         }
         const float qs = p == 0 ? a.q_scale : 1.0f;
         u32x4 o0, o1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            o0[e] = pack16<DT>(v[u][2 * e] * qs, v[u][2 * e + 1] * qs);
-            o1[e] = pack16<DT>(v[u][8 + 2 * e] * qs, v[u][8 + 2 * e + 1] * qs);
+            o0[e] = pack16<DT>(v[2 * e] * qs, v[2 * e + 1] * qs);
+            o1[e] = pack16<DT>(v[8 + 2 * e] * qs, v[8 + 2 * e + 1] * qs);
         }
         dst = p == 0 ? (char*)a.q_out + (t * a.Hq + hl) * (int64_t)D * 2
                      : (char*)a.k_out + (t * a.Hkv + hl) * (int64_t)D * 2;
