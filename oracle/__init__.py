@@ -97,6 +97,9 @@ def lib():
         L.oracle_resid_rmsnorm_mxfp4.restype = _INT
         L.oracle_gated_act_mxfp4.argtypes = [_P, _INT, _P, _P, _I64, _I64, _INT]
         L.oracle_gated_act_mxfp4.restype = _INT
+        L.oracle_resid_layernorm.argtypes = [
+            _P, _P, _P, _P, _P, _F, _INT, _P, _INT, _F, _P, _P, _I64, _I64, _INT]
+        L.oracle_resid_layernorm.restype = _INT
         L.or_layernorm.argtypes = [_P, _P, _P, _I64, _D, _P]
         L.or_layernorm.restype = None
         L.or_rope3d.argtypes = [_P, _I64, _P, _P, _D, _INT]
@@ -400,6 +403,31 @@ def rope3d(v, pos3, sections, theta, style=ROPE_HALF):
     sec = np.ascontiguousarray(sections, dtype=np.int32)
     lib().or_rope3d(_ptr(v), v.size, _ptr(p), _ptr(sec), float(theta), style)
     return v
+
+
+def resid_layernorm(x, residual, weight, bias, eps, out_kind, qmode, static_scale,
+                    dtype):
+    """out_kind 0 (FP8): returns (residual_out, codes [T,H], scales [T] or None);
+    out_kind 1 (MXFP4): returns (residual_out, packed [T,H/2], e8m0 [T,H/32])."""
+    x = _c(x, np.uint16)
+    residual = _c(residual, np.uint16)
+    T, H = x.shape
+    weight = _c(weight, np.uint16)
+    bias = _c(bias, np.uint16)
+    ro = np.empty_like(x)
+    if out_kind == 1:
+        q = np.empty((T, H // 2), np.uint8)
+        sc8 = np.empty((T, H // 32), np.uint8)
+        scf = None
+    else:
+        q = np.empty((T, H), np.uint8)
+        sc8 = None
+        scf = np.empty(T, np.float32) if qmode == Q_TOKEN else None
+    rc = lib().oracle_resid_layernorm(
+        _ptr(x), _ptr(residual), _ptr(ro), _ptr(weight), _ptr(bias), eps, out_kind,
+        _ptr(q), qmode, static_scale, _ptr(scf), _ptr(sc8), T, H, dtype)
+    assert rc == 0
+    return ro, q, (sc8 if out_kind == 1 else scf)
 
 
 def qk_norm_rope(qkv, norm_kind, norm_scope, q_norm_w, q_norm_b, k_norm_w,

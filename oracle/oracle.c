@@ -478,6 +478,54 @@ int oracle_resid_rmsnorm_mxfp4(const uint16_t* x, const uint16_t* residual,
     return 0;
 }
 
+/* Residual add + LayerNorm + FP8 or MX FP4 [HY 06 census: the ViT
+ * add-LayerNorm FP4 producer; the FP8 output as in the RMSNorm op]:
+ *   residual_out = round(x + residual); y = LayerNorm(residual_out) with
+ *   weight and bias (bias may be NULL);
+ *   out_kind 0: FP8, static (code = E(y * static_scale)) or per token
+ *   (qmode 1: scale = amax / 448 into out_scales_f32);
+ *   out_kind 1: MXFP4 blocks of 32 (out_codes [T, H/2], out_scales_e8m0
+ *   [T, H/32]). */
+int oracle_resid_layernorm(const uint16_t* x, const uint16_t* residual,
+                           uint16_t* residual_out, const uint16_t* weight,
+                           const uint16_t* bias, float eps, int out_kind,
+                           uint8_t* out_codes, int qmode, float static_scale,
+                           float* out_scales_f32, uint8_t* out_scales_e8m0,
+                           int64_t T, int64_t H, int dtype)
+{
+    if (out_kind == 1 && H % 32 != 0)
+        return -2;
+    double* ro = malloc(sizeof(double) * (size_t)H);
+    double* w = malloc(sizeof(double) * (size_t)H);
+    double* b = malloc(sizeof(double) * (size_t)H);
+    double* y = malloc(sizeof(double) * (size_t)H);
+    if (!ro || !w || !b || !y) {
+        free(ro); free(w); free(b); free(y);
+        return -1;
+    }
+    for (int64_t j = 0; j < H; ++j) {
+        w[j] = dec16(weight[j], dtype);
+        b[j] = bias ? dec16(bias[j], dtype) : 0.0;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t j = 0; j < H; ++j) {
+            uint16_t c = enc16(dec16(x[t * H + j], dtype) + dec16(residual[t * H + j], dtype),
+                               dtype);
+            residual_out[t * H + j] = c;
+            ro[j] = dec16(c, dtype);
+        }
+        or_layernorm(ro, w, b, H, (double)eps, y);
+        if (out_kind == 1)
+            or_quant_mxfp4(y, H, out_codes + t * (H / 2), out_scales_e8m0 + t * (H / 32));
+        else if (qmode == OR_Q_STATIC)
+            or_quant_static(y, H, (double)static_scale, out_codes + t * H);
+        else
+            out_scales_f32[t] = or_quant_dynamic(y, H, out_codes + t * H);
+    }
+    free(ro); free(w); free(b); free(y);
+    return 0;
+}
+
 /* Gate multiply + residual + adaptive RMSNorm + FP8 [FR section 三]:
  *   residual_out = round(residual + gate * x)
  *   y = RMSNorm(residual_out) * (1 + ada_scale) + ada_shift

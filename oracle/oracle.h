@@ -107,6 +107,12 @@ int oracle_resid_rmsnorm_mxfp4(const uint16_t* x, const uint16_t* residual,
                                int wmode, float eps, uint8_t* out_fp4,
                                uint8_t* out_scales, int64_t T, int64_t H,
                                int dtype);
+int oracle_resid_layernorm(const uint16_t* x, const uint16_t* residual,
+                           uint16_t* residual_out, const uint16_t* weight,
+                           const uint16_t* bias, float eps, int out_kind,
+                           uint8_t* out_codes, int qmode, float static_scale,
+                           float* out_scales_f32, uint8_t* out_scales_e8m0,
+                           int64_t T, int64_t H, int dtype);
 int oracle_gated_act_mxfp4(const uint16_t* gate_up, int act, uint8_t* out_fp4,
                            uint8_t* out_scales, int64_t T, int64_t I, int dtype);
 int oracle_qk_norm_rope(const uint16_t* qkv, int norm_kind, int norm_scope,

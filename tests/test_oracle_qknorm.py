@@ -126,3 +126,29 @@ def test_op_composes_pinned_pieces(kind, scope, dims):
                      else oracle.rope(yh, int(pos[t]), 1e4, oracle.ROPE_INTERLEAVED))
                 assert np.array_equal(out[t, h], oracle.encode16_n(r, dt))
         assert np.array_equal(v[t].reshape(-1), qkv[t, (Hq + Hkv) * D:])
+
+
+@pytest.mark.parametrize("out_kind,qmode", [(0, oracle.Q_STATIC), (0, oracle.Q_TOKEN), (1, 0)])
+def test_resid_layernorm_composes_pinned_pieces(out_kind, qmode):
+    dt = oracle.BF16
+    T, H = 3, 256
+    inp = workloads.resid_rmsnorm_inputs(T, H, dt, seed=40, outliers=True)
+    rng = np.random.default_rng(41)
+    bias = workloads.to16(0.1 * rng.standard_normal(H).astype(np.float32), dt)
+    ro, q, sc = oracle.resid_layernorm(inp["x"], inp["residual"], inp["weight"], bias, EPS,
+                                       out_kind, qmode, 56.0, dt)
+    ro8, _, _ = oracle.resid_rmsnorm_fp8(inp["x"], inp["residual"], None, oracle.W_NONE,
+                                         EPS, oracle.Q_STATIC, 1.0, dt)
+    assert np.array_equal(ro, ro8)
+    w, b = oracle.decode16(inp["weight"], dt), oracle.decode16(bias, dt)
+    for t in range(T):
+        y = oracle.layernorm(oracle.decode16(ro[t], dt), w, b, EPS)
+        if out_kind == 1:
+            pw, sw = oracle.quant_mxfp4(y)
+            assert np.array_equal(q[t], pw) and np.array_equal(sc[t], sw)
+        elif qmode == oracle.Q_STATIC:
+            assert np.array_equal(q[t], oracle.e4m3_encode_n(y * 56.0))
+        else:
+            s = np.float32(max(np.abs(y).max(), np.float32(1e-10)) / 448.0)
+            assert sc[t] == s
+            assert np.array_equal(q[t], oracle.e4m3_encode_n(y / np.float64(s)))
