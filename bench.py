@@ -509,9 +509,19 @@ def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
         fr.fr_gated_act_mxfp4(d["gu"], fr.ACT_SWIGLU, d["q"], d["s"], T, I,
                               fr.BF16, stream=stream)
 
+    # the add + LayerNorm producer (ViT style): weight and bias, same rows
+    bias = dev(workloads.to16(np.full(H, 0.01, np.float32), workloads.BF16))
+    nb_ln = nb_norm + H * 2
+
+    def ln(i):
+        d = N[i % len(N)]
+        fr.fr_resid_layernorm_mxfp4(d["x"], d["residual"], d["ro"], d["weight"], bias,
+                                    EPS, d["q"], d["s"], T, H, fr.BF16, stream=stream)
+
     out = {}
     for name, f, nb in (("resid_rmsnorm_mxfp4_T8192_H4096", norm, nb_norm),
-                        ("gated_act_mxfp4_T8192_I12288", act, nb_act)):
+                        ("gated_act_mxfp4_T8192_I12288", act, nb_act),
+                        ("resid_layernorm_mxfp4_T8192_H4096", ln, nb_ln)):
         for i in range(3):
             f(i)
         torch.cuda.synchronize()

@@ -217,6 +217,31 @@ int fr_resid_rmsnorm_mxfp4(const void* x, const void* residual,
                            int64_t T, int64_t H, int dtype, void* stream);
 
 /*
+ * (a-ln) residual add + LayerNorm + FP8 or MXFP4 [HY 06 census: the ViT
+ *   add + LayerNorm FP4 producer; FR 二 table step 1 for the fused FP8 form]
+ *
+ *   residual_out = round_dtype(x + residual) (bit-exact, as op (a));
+ *   y = (residual_out - mean) / sqrt(var + eps) * weight + bias, mean and
+ *   biased variance over the row (fp64 sums of the stored values), y in
+ *   fp32; bias may be NULL (0).
+ *   _fp8: quantised as fr_resid_rmsnorm_fp8 (FR_Q_STATIC multiplier or
+ *   FR_Q_TOKEN scale); out_fp8 [T,H], out_scales [T] (token mode).
+ *   _mxfp4: MXFP4 as fr_resid_rmsnorm_mxfp4; out_fp4 [T,H/2], out_scales
+ *   [T,H/32]; H % 32 == 0.
+ *   weight: [H] required; all tensors 16-byte aligned.
+ */
+int fr_resid_layernorm_fp8(const void* x, const void* residual,
+                           void* residual_out, const void* weight,
+                           const void* bias, float eps, uint8_t* out_fp8,
+                           int qmode, float static_scale, float* out_scales,
+                           int64_t T, int64_t H, int dtype, void* stream);
+int fr_resid_layernorm_mxfp4(const void* x, const void* residual,
+                             void* residual_out, const void* weight,
+                             const void* bias, float eps, uint8_t* out_fp4,
+                             uint8_t* out_scales, int64_t T, int64_t H,
+                             int dtype, void* stream);
+
+/*
  * (c-fp4) gated activation + MXFP4: h = act(g) * u as fr_gated_act_fp8 (fp32
  *   activation), quantised in blocks of 32 outputs.  out_fp4: [T, I/2]
  *   bytes (16-byte aligned); out_scales: [T, I/32] bytes.  I % 128 == 0.

@@ -60,6 +60,10 @@ _SIGS = {
     "fr_resid_rmsnorm_mxfp4": [_P, _P, _P, _P, _INT, _F, _P, _P, _I64, _I64,
                                _INT, _P],
     "fr_gated_act_mxfp4": [_P, _INT, _P, _P, _I64, _I64, _INT, _P],
+    "fr_resid_layernorm_fp8": [_P, _P, _P, _P, _P, _F, _P, _INT, _F, _P, _I64,
+                               _I64, _INT, _P],
+    "fr_resid_layernorm_mxfp4": [_P, _P, _P, _P, _P, _F, _P, _P, _I64, _I64,
+                                 _INT, _P],
     "fr_qk_norm_rope": [_P, _INT, _INT, _P, _P, _P, _P, _F, _P, _INT, _I32,
                         _I32, _I32, _F, _INT, _F, _P, _P, _P, _I64, _I32, _I32,
                         _I32, _INT, _P],
@@ -197,6 +201,22 @@ def fr_decode_chain_persistent(x, gate, ada_scale, ada_shift, residual,
         rope_theta, rope_style, _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
         _ptr(page_table), page_table_len, page_size, num_pages, _ptr(err_flag),
         layers, steps, T, H, Hq, Hkv, D, dtype, _stream(stream)))
+
+
+def fr_resid_layernorm_fp8(x, residual, residual_out, weight, bias, eps,
+                           out_fp8, qmode, static_scale, out_scales, T, H,
+                           dtype, stream=None):
+    _check(lib.fr_resid_layernorm_fp8(
+        _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(weight), _ptr(bias),
+        eps, _ptr(out_fp8), qmode, static_scale, _ptr(out_scales), T, H, dtype,
+        _stream(stream)))
+
+
+def fr_resid_layernorm_mxfp4(x, residual, residual_out, weight, bias, eps,
+                             out_fp4, out_scales, T, H, dtype, stream=None):
+    _check(lib.fr_resid_layernorm_mxfp4(
+        _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(weight), _ptr(bias),
+        eps, _ptr(out_fp4), _ptr(out_scales), T, H, dtype, _stream(stream)))
 
 
 def fr_qk_norm_rope(qkv, norm_kind, norm_scope, q_norm_w, q_norm_b, k_norm_w,

@@ -15,7 +15,8 @@ struct NormArgs {
     const void* gate;       // [T,H]   (adaptive variant only)
     const void* res;        // [T,H]
     void* res_out;          // [T,H]
-    const void* w;          // [H]     (plain variant, FR_W_MUL / FR_W_ONE_PLUS)
+    const void* w;          // [H]     (plain variant, FR_W_MUL / FR_W_ONE_PLUS; LayerNorm)
+    const void* b;          // [H]     (LayerNorm bias, may be NULL)
     const void* ada_scale;  // [T,H]   (adaptive variant only)
     const void* ada_shift;  // [T,H]   (adaptive variant only)
     uint8_t* out;           // [T,H] FP8, or [T,H/2] MX FP4
@@ -139,7 +140,7 @@ struct QkNormArgs {
 };
 hipError_t launch_qknr(const QkNormArgs& a, int dtype, hipStream_t s);
 
-enum { NORM_FP8 = 0, NORM_ADA_FP8 = 1, NORM_MXFP4 = 2 };
+enum { NORM_FP8 = 0, NORM_ADA_FP8 = 1, NORM_MXFP4 = 2, NORM_LAYER_FP8 = 3, NORM_LAYER_MXFP4 = 4 };
 hipError_t launch_norm(const NormArgs& a, int dtype, int kind, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int dtype, hipStream_t s);
 hipError_t launch_act(const ActArgs& a, int dtype, int act, bool mx, hipStream_t s);

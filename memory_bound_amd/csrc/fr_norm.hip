@@ -42,7 +42,7 @@
 
 namespace fr {
 
-enum { M_NONE = 0, M_MUL = 1, M_ONE_PLUS = 2, M_ADA = 3 };
+enum { M_NONE = 0, M_MUL = 1, M_ONE_PLUS = 2, M_ADA = 3, M_LAYER = 4 };
 
 template <bool NT>
 __device__ __forceinline__ u32x4 ld_in(const void* p) {
@@ -62,8 +62,10 @@ __device__ __forceinline__ void st_out(void* p, u32x2 v) {
 template <int DT, int CPL, int MODE, bool NTL, bool NTS = NTL, bool MX = false>
 __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     constexpr bool ADA = MODE == M_ADA;
-    constexpr bool HAS_W = MODE == M_MUL || MODE == M_ONE_PLUS;
+    constexpr bool LAYER = MODE == M_LAYER;
+    constexpr bool HAS_W = MODE == M_MUL || MODE == M_ONE_PLUS || LAYER;
     __shared__ double red_ss[8];
+    __shared__ double red_ss2[8];
     __shared__ float red_max[8];
 
     const int lane = threadIdx.x & 63;
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     const char* rr = (const char*)a.res + rb;
     char* ror = (char*)a.res_out + rb;
 
-    u32x4 xv[CPL], rv[CPL], gv[CPL], sv[CPL], hv[CPL], wv[CPL];
+    u32x4 xv[CPL], rv[CPL], gv[CPL], sv[CPL], hv[CPL], wv[CPL], bv[CPL];
     bool ok[CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
@@ -96,6 +98,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
             hv[k] = ld_in<NTL>((const char*)a.ada_shift + rb + cl * 16);
         }
         if constexpr (HAS_W) wv[k] = ld128((const char*)a.w + cl * 16);
+        if constexpr (LAYER) bv[k] = a.b ? ld128((const char*)a.b + cl * 16) : (u32x4){0, 0, 0, 0};
     }
 
     // Pass 1: new residual, rounded once; sum of squares of the stored value.
@@ -129,6 +132,101 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
         }
     }
 
+    uint8_t* orow = a.out + t * (int64_t)a.H;
+    if constexpr (LAYER) {
+        // LayerNorm: mean, then the variance about it, both as fp64 row sums
+        // of the stored values (exact for realistic rows, so independent of
+        // the order); y = (ro - mean) * rstd * w + b in fp32.
+        auto row_sum = [&](double v, double* slots) {
+            v = wave_sum_d(v);
+            if (a.nw > 1) {
+                if (lane == 0) slots[wave] = v;
+                __syncthreads();
+                v = slots[rw * a.nw];
+                for (int w = 1; w < a.nw; ++w) v += slots[rw * a.nw + w];
+            }
+            return v;
+        };
+        double s1 = 0.0;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            if (!ok[k]) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                s1 += (double)lo16<DT>(rv[k][e]) + (double)hi16<DT>(rv[k][e]);
+        }
+        const double mean_d = row_sum(s1, red_ss) / (double)a.H;
+        double s2 = 0.0;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            if (!ok[k]) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double d0 = (double)lo16<DT>(rv[k][e]) - mean_d;
+                const double d1 = (double)hi16<DT>(rv[k][e]) - mean_d;
+                s2 = fma(d0, d0, fma(d1, d1, s2));
+            }
+        }
+        const double var_d = row_sum(s2, red_ss2) / (double)a.H;
+        const float rstd = (float)(1.0 / sqrt(var_d + (double)a.eps));
+        const float mean = (float)mean_d;
+        float y[CPL][8];
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y[k][2 * e] = fmaf((lo16<DT>(rv[k][e]) - mean) * rstd, lo16<DT>(wv[k][e]),
+                                   lo16<DT>(bv[k][e]));
+                y[k][2 * e + 1] = fmaf((hi16<DT>(rv[k][e]) - mean) * rstd, hi16<DT>(wv[k][e]),
+                                       hi16<DT>(bv[k][e]));
+                if (ok[k]) amax = fmaxf(amax, fmaxf(fabsf(y[k][2 * e]), fabsf(y[k][2 * e + 1])));
+            }
+        }
+        if constexpr (MX) {
+            uint8_t* orow4 = a.out + t * (int64_t)(a.H >> 1);
+            uint8_t* srow = a.mx_scales + t * (int64_t)(a.H >> 5);
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                float m = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(y[k][e]));
+                m = group_reduce<4>(m, OpMax());         // a block of 32 = 4 lanes
+                const int code = mx_code(m);
+                const u32 p = pack_e2m1x8(y[k], mx_mult(code));
+                if (ok[k] && row_ok) {
+                    const int c = k * stride + ww * 64 + lane;
+                    u32* dst = (u32*)(orow4 + c * 4);
+                    if constexpr (NTS) __builtin_nontemporal_store(p, dst); else *dst = p;
+                    if ((lane & 3) == 0) srow[c >> 2] = (uint8_t)code;
+                }
+            }
+            return;
+        }
+        float mult = a.static_scale;
+        if (a.qmode == 1) {
+            amax = wave_reduce(amax, OpMax());
+            if (a.nw > 1) {
+                if (lane == 0) red_max[wave] = amax;
+                __syncthreads();
+                amax = red_max[rw * a.nw];
+                for (int w = 1; w < a.nw; ++w) amax = fmaxf(amax, red_max[rw * a.nw + w]);
+            }
+            const float s = (float)((double)fmaxf(amax, 1e-10f) / 448.0);
+            mult = 1.0f / s;
+            if (row_ok && ww == 0 && lane == 0) a.scales[t] = s;
+        }
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            if (!ok[k] || !row_ok) continue;
+            u32x2 q;
+            q.x = pack_e4m3x4(y[k][0] * mult, y[k][1] * mult, y[k][2] * mult, y[k][3] * mult);
+            q.y = pack_e4m3x4(y[k][4] * mult, y[k][5] * mult, y[k][6] * mult, y[k][7] * mult);
+            st_out<NTS>(orow + (k * stride + ww * 64 + lane) * 8, q);
+        }
+        return;
+    }
+
     double ss = wave_sum_d(ss0 + ss1);
     if (a.nw > 1) {
         if (lane == 0) red_ss[wave] = ss;
@@ -137,7 +235,6 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
         for (int w = 1; w < a.nw; ++w) ss += red_ss[rw * a.nw + w];
     }
     const double rstd_d = 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
-    uint8_t* orow = a.out + t * (int64_t)a.H;
 
     if constexpr (ADA) {
         // Pass 2 (adaptive): y = n * (1 + scale) + shift in fp32.
@@ -291,6 +388,7 @@ static hipError_t launch_norm_dt(const NormArgs& a, int mode, bool mx, int cpl, 
         switch (mode) {
         case M_NONE: return launch_norm_mode<DT, M_NONE, NT, true>(a, cpl, s);
         case M_MUL: return launch_norm_mode<DT, M_MUL, NT, true>(a, cpl, s);
+        case M_LAYER: return launch_norm_mode<DT, M_LAYER, NT, true>(a, cpl, s);
         default: return launch_norm_mode<DT, M_ONE_PLUS, NT, true>(a, cpl, s);
         }
     }
@@ -298,6 +396,7 @@ static hipError_t launch_norm_dt(const NormArgs& a, int mode, bool mx, int cpl, 
     case M_NONE: return launch_norm_mode<DT, M_NONE, NT, false>(a, cpl, s);
     case M_MUL: return launch_norm_mode<DT, M_MUL, NT, false>(a, cpl, s);
     case M_ONE_PLUS: return launch_norm_mode<DT, M_ONE_PLUS, NT, false>(a, cpl, s);
+    case M_LAYER: return launch_norm_mode<DT, M_LAYER, NT, false>(a, cpl, s);
     default: return launch_norm_mode<DT, M_ADA, NT, false>(a, cpl, s);
     }
 }
@@ -333,11 +432,12 @@ static NormShape pick_norm_shape(int64_t T, int H, bool adaptive) {
 hipError_t launch_norm(const NormArgs& in, int dtype, int kind, hipStream_t s) {
     NormArgs a = in;
     const bool adaptive = kind == NORM_ADA_FP8;
-    const bool mx = kind == NORM_MXFP4;
+    const bool layer = kind == NORM_LAYER_FP8 || kind == NORM_LAYER_MXFP4;
+    const bool mx = kind == NORM_MXFP4 || kind == NORM_LAYER_MXFP4;
     const NormShape sh = pick_norm_shape(a.T, a.H, adaptive);
     a.nw = sh.nw;
     a.rpb = sh.rpb;
-    const int mode = adaptive ? M_ADA : a.wmode;
+    const int mode = adaptive ? M_ADA : (layer ? M_LAYER : a.wmode);
     if (dtype == DT_BF16)
         return sh.nt ? launch_norm_dt<DT_BF16, true>(a, mode, mx, sh.cpl, s)
                      : launch_norm_dt<DT_BF16, false>(a, mode, mx, sh.cpl, s);

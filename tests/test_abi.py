@@ -29,8 +29,8 @@ def test_header_declares_the_four_ops_and_helpers():
         "fr_resid_rmsnorm_fp8", "fr_adarms_gate_res_fp8",
         "fr_qkv_normrope_kvwrite", "fr_gated_act_fp8", "fr_gemm_gated_act_fp8",
         "fr_gemm_pack_weights", "fr_resid_rmsnorm_mxfp4", "fr_gated_act_mxfp4",
-        "fr_decode_chain_persistent", "fr_qk_norm_rope", "fr_status_string",
-        "fr_abi_version"])
+        "fr_decode_chain_persistent", "fr_qk_norm_rope", "fr_resid_layernorm_fp8",
+        "fr_resid_layernorm_mxfp4", "fr_status_string", "fr_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -303,3 +303,25 @@ def test_qk_norm_rope_validation(kw, status):
     if kw.get("rope_dims") == 3 and kw.get("sec_t") == 22:
         kw["T"] = 0                       # valid sections; launch nothing
     assert qknr(**kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, None, None, 1e-6, E, 0, 56.0, None, 10, 1024, fr.F16), fr.FR_ERR_NULL),
+    ((A, B, C, D_, G + 2, 1e-6, E, 0, 56.0, None, 10, 1024, fr.F16), fr.FR_ERR_ALIGN),
+    ((A, B, C, D_, None, 1e-6, E, 1, 0.0, None, 10, 1024, fr.F16), fr.FR_ERR_NULL),
+    ((A, B, C, D_, None, 1e-6, E, 0, 56.0, None, 10, 1000, fr.F16), fr.FR_ERR_SHAPE),
+    ((A, B, C, D_, G, 1e-6, E, 0, 56.0, None, 0, 1024, fr.F16), fr.FR_OK),
+])
+def test_resid_layernorm_fp8_validation(args, status):
+    assert fr.lib.fr_resid_layernorm_fp8(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, None, None, 1e-6, E, F, 10, 1024, fr.F16), fr.FR_ERR_NULL),
+    ((A, B, C, D_, None, 1e-6, E, None, 10, 1024, fr.F16), fr.FR_ERR_NULL),
+    ((A, B, C, D_, None, 1e-6, E, F, 10, 1040, fr.F16), fr.FR_ERR_SHAPE),
+    ((A, B, C, D_, None, 1e-6, E + 8, F, 10, 1024, fr.F16), fr.FR_ERR_ALIGN),
+    ((A, B, C, D_, G, 1e-6, E, F, 0, 1024, fr.F16), fr.FR_OK),
+])
+def test_resid_layernorm_mxfp4_validation(args, status):
+    assert fr.lib.fr_resid_layernorm_mxfp4(*args, None) == status

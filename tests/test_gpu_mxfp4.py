@@ -83,3 +83,53 @@ def test_gated_act_mxfp4_every_byte_written(fr):
     b = run_gated_act_mxfp4(fr, inp, oracle.ACT_SWIGLU, BF16, poison=0xFF)
     for x, y in zip(a, b):
         check_exact(x, y, "poison-independent output")
+
+
+# ---------------------------------------------------------------------------
+# residual add + LayerNorm producers (FP8 and MXFP4)
+# ---------------------------------------------------------------------------
+
+LN_CASES = [
+    # (name, T, H, dtype, out_kind, qmode, bias, seed)
+    ("vit_mx_1024", 64, 1024, BF16, 1, 0, True, 521),
+    ("vit_mx_nobias_f16", 10, 2048, F16, 1, 0, False, 522),
+    ("fp8_token_4096", 128, 4096, BF16, 0, 1, True, 523),
+    ("fp8_static_1056", 17, 1056, F16, 0, 0, True, 524),
+    ("mx_32768", 3, 32768, BF16, 1, 0, True, 525),
+    ("mx_bench_8192", 8192, 4096, BF16, 1, 0, True, 526),
+]
+
+
+@pytest.mark.parametrize("case", LN_CASES, ids=lambda c: c[0])
+def test_resid_layernorm(fr, case):
+    import torch
+    from parity import POISON16, check_fp8, check_scales, to_dev, to_host
+    name, T, H, dt, kind, qmode, has_b, seed = case
+    announce(f"resid_layernorm {name} T={T} H={H} kind={kind} qmode={qmode}")
+    inp = workloads.resid_rmsnorm_inputs(T, H, dt, seed, outliers=True)
+    rng = np.random.default_rng(seed + 1)
+    bias = workloads.to16(0.1 * rng.standard_normal(H).astype(np.float32), dt) if has_b else None
+    x, r, w = to_dev(inp["x"]), to_dev(inp["residual"]), to_dev(inp["weight"])
+    b = to_dev(bias) if has_b else None
+    ro = torch.full((T, H), POISON16, dtype=torch.int16, device="cuda")
+    if kind == 1:
+        q = torch.full((T, H // 2), 0xAA, dtype=torch.uint8, device="cuda")
+        sc = torch.full((T, H // 32), 0xFF, dtype=torch.uint8, device="cuda")
+        fr.fr_resid_layernorm_mxfp4(x, r, ro, w, b, EPS, q, sc, T, H, dt)
+    else:
+        q = torch.full((T, H), 0x7F, dtype=torch.uint8, device="cuda")
+        sc = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+        fr.fr_resid_layernorm_fp8(x, r, ro, w, b, EPS, q, qmode, 40.0, sc, T, H, dt)
+    torch.cuda.synchronize()
+    ro_o, q_o, s_o = oracle.resid_layernorm(inp["x"], inp["residual"], inp["weight"], bias,
+                                            EPS, kind, qmode, 40.0, dt)
+    check_exact(to_host(ro, np.uint16), ro_o, "residual_out")
+    if kind == 1:
+        ident, frac = check_fp4(to_host(q, np.uint8), to_host(sc, np.uint8), q_o, s_o,
+                                "resid_layernorm_mxfp4")
+        announce(f"  codes identical {ident:.6f}, block scales differing {frac:.2e}")
+    else:
+        ident = check_fp8(to_host(q, np.uint8), q_o, "out_fp8")
+        if qmode == 1:
+            check_scales(to_host(sc, np.float32), s_o, "out_scales")
+        announce(f"  fp8 identical {ident:.6f}")
