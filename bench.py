@@ -193,7 +193,7 @@ def main():
                     f(i)
         torch.cuda.synchronize()
         run_mxfp4(torch, fr, workloads, dev, stream, 3, timed=False)
-        run_qknorm(torch, fr, workloads, dev, stream, 3, timed=False)
+        run_qknorm(torch, fr, workloads, dev, stream, 3, timed=False, only="wan")
         run_gemm_act(torch, fr, workloads, dev, stream, reps=3, timed=False,
                      shapes=((128, 2048, 6144),))
         print(json.dumps({"pmc_pass": True, "copy_bytes_each_way": 1 << 30,
@@ -546,7 +546,7 @@ def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
     return out
 
 
-def run_qknorm(torch, fr, workloads, dev, stream, reps, timed=True):
+def run_qknorm(torch, fr, workloads, dev, stream, reps, timed=True, only=None):
     """fr_qk_norm_rope at 8192 tokens: the Wan-style full-width RMSNorm + 3D
     RoPE (40/40 heads x 128 bf16) and the Chameleon-style LayerNorm per head
     + RoPE (32/32 heads x 128 bf16); buffers rotated through >= 512 MB."""
@@ -555,6 +555,8 @@ def run_qknorm(torch, fr, workloads, dev, stream, reps, timed=True):
     for name, Hq, Hkv, kind, full, r3, sec, style in (
             ("wan_rms_full_3d_T8192_40x128", 40, 40, fr.NORM_RMS, True, True, (22, 21, 21), 1),
             ("chameleon_layer_head_T8192_32x128", 32, 32, fr.NORM_LAYER, False, False, None, 0)):
+        if only is not None and not name.startswith(only):
+            continue
         NH = Hq + 2 * Hkv
         nb = 2 * T * NH * D * 2 + 4 * T * (3 if r3 else 1)
         inp = workloads.qk_norm_rope_inputs(T, Hq, Hkv, D, workloads.BF16, 610,

@@ -47,6 +47,12 @@ KERNELS = {  # kernel name prefix -> (op, algorithmic read bytes, write bytes)
     "void fr::k_act<1, 0, 8, true, false, true>": (
         "gated_act_mxfp4 T=8192 I=12288 bf16 SwiGLU",
         8192 * 24576 * 2, 8192 * 6144 + 8192 * 384),
+    "void fr::k_norm<1, 2, 4, true, true, true>": (
+        "resid_layernorm_mxfp4 T=8192 H=4096 bf16",
+        8192 * 4096 * 4 + 4096 * 4, 8192 * 4096 * 2 + 8192 * 2048 + 8192 * 128),
+    "void fr::k_qknr<1, 8, 4>": (
+        "qk_norm_rope T=8192 40/40x128 bf16 RMS full 3D (Wan)",
+        8192 * 120 * 128 * 2 + 8192 * 12 + 2 * 5120 * 2 * 2, 8192 * 120 * 128 * 2),
     "void fr::k_gemm_act<0, 1, 2>": (
         "gemm_gated_act_fp8 M=128 K=2048 I=6144 (weight, A, scales)",
         12288 * 2048 + 128 * 2048 + 128 * 16 * 4 + 96 * 16 * 4,
