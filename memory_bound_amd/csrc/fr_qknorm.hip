@@ -78,6 +78,13 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
         return (e & 1) ? hi16<DT>(w) : lo16<DT>(w);
     };
     auto part = [&](int h) { return h < a.Hq ? 0 : (h < a.Hq + a.Hkv ? 1 : 2); };  // Q, K, V
+    // Between passes over the heads the raw registers are marked as changed,
+    // so each pass widens its values afresh instead of keeping all of them
+    // widened (four times the registers) from the previous pass.
+    auto fence_raw = [&]() {
+#pragma unroll
+        for (int u = 0; u < U; ++u) asm volatile("" : "+v"(c0[u]), "+v"(c1[u]));
+    };
 
     // ---- norm statistics (per unit: mean[u], rstd[u]) ----
     float mean[U], rstd[U];
@@ -92,12 +99,14 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
             if (layer) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    double s = 0.0;
+                    float su = 0.0f;                     // 16 values: fp32 is ample
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) s += (double)val(u, e);
+                    for (int e = 0; e < 16; ++e) su += val(u, e);
+                    const double s = (double)su;
                     const int p = part(head[u]);
                     if (p == 0) sq += s; else if (p == 1) sk += s;
                 }
+                fence_raw();
                 sq = wave_sum_d(sq);
                 sk = wave_sum_d(sk);
                 if (lane == 0) { red[wv][0] = sq; red[wv][1] = sk; }
@@ -109,14 +118,14 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int p = part(head[u]);
-                const double m = p == 0 ? mq : mk;
-                double s = 0.0;
+                const float m = (float)(p == 0 ? mq : mk);
+                float su = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const double d = (double)val(u, e) - m;
-                    s = fma(d, d, s);
+                    const float d = val(u, e) - m;
+                    su = fmaf(d, d, su);
                 }
-                if (!lane_ok) s = 0.0;
+                const double s = lane_ok ? (double)su : 0.0;
                 if (p == 0) sq += s; else if (p == 1) sk += s;
             }
             sq = wave_sum_d(sq);
@@ -159,6 +168,7 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
         }
     }
 
+    fence_raw();
     __syncthreads();                                     // angle table complete
 
     // ---- apply, rotate, store ----
@@ -232,6 +242,7 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
                      : (char*)a.k_out + (t * a.Hkv + hl) * (int64_t)D * 2;
         st128_stream(dst + off0, o0);
         st128_stream(dst + off1, o1);
+        __builtin_amdgcn_sched_barrier(0);               // one unit's temporaries at a time
     }
 }
 
