@@ -137,6 +137,7 @@ struct QkNormArgs {
     int sec[3];             // 3D RoPE pairs per axis
     int style;
     float eps, theta, q_scale;
+    double inv_nq, inv_nk;  // 1 / (Hq D), 1 / (Hkv D): set by launch_qknr
 };
 hipError_t launch_qknr(const QkNormArgs& a, int dtype, hipStream_t s);
 

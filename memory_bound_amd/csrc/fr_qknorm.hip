@@ -14,15 +14,17 @@
 // pair -- rotate-half (i, i + D/2) or interleaved (2i, 2i+1) -- sits in one
 // lane.  The token's heads are covered in U passes of 256/LP heads, all
 // loaded before any arithmetic and kept in registers, so a full-width norm
-// needs no second read: its sums are a wave reduction plus one LDS step
-// (fp64, so they do not depend on the order).  A per-head norm is a DPP
+// needs no second read: each thread sums its 16 values per head in fp32,
+// then a wave reduction and one LDS step add the partial sums in fp64 (so
+// the total barely depends on the order).  A per-head norm is a DPP
 // reduction over the head's lanes.  LayerNorm subtracts the mean first
 // (two reductions).  The token's D/2 rotation angles are computed once per
 // workgroup (one per thread, fp64 as in op b) into LDS and serve every
 // head; 3D RoPE splits the pairs into time / height / width ranges, each
 // turned by its own position.  Heads stay in registers as raw 16-bit pairs
-// and are widened on use (one shift or convert each), which keeps four
-// passes of heads within 128 registers.
+// and are widened on use (one shift or convert each), each pass widening
+// afresh, which keeps four passes of heads within 96 registers: five
+// workgroups (five tokens) per CU in flight.
 #include "fr_device.h"
 #include "fr_launch.h"
 
@@ -111,8 +113,8 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
                 sk = wave_sum_d(sk);
                 if (lane == 0) { red[wv][0] = sq; red[wv][1] = sk; }
                 __syncthreads();
-                mq = (red[0][0] + red[1][0] + red[2][0] + red[3][0]) / ((double)a.Hq * D);
-                mk = (red[0][1] + red[1][1] + red[2][1] + red[3][1]) / ((double)a.Hkv * D);
+                mq = (red[0][0] + red[1][0] + red[2][0] + red[3][0]) * a.inv_nq;
+                mk = (red[0][1] + red[1][1] + red[2][1] + red[3][1]) * a.inv_nk;
                 sq = sk = 0.0;
             }
 #pragma unroll
@@ -132,10 +134,10 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
             sk = wave_sum_d(sk);
             if (lane == 0) { red[wv][2] = sq; red[wv][3] = sk; }
             __syncthreads();
-            const double vq = (red[0][2] + red[1][2] + red[2][2] + red[3][2]) / ((double)a.Hq * D);
-            const double vk = (red[0][3] + red[1][3] + red[2][3] + red[3][3]) / ((double)a.Hkv * D);
-            const float rq = (float)(1.0 / sqrt(vq + (double)a.eps));
-            const float rk = (float)(1.0 / sqrt(vk + (double)a.eps));
+            const double vq = (red[0][2] + red[1][2] + red[2][2] + red[3][2]) * a.inv_nq;
+            const double vk = (red[0][3] + red[1][3] + red[2][3] + red[3][3]) * a.inv_nk;
+            const float rq = 1.0f / sqrtf((float)vq + a.eps);
+            const float rk = 1.0f / sqrtf((float)vk + a.eps);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int p = part(head[u]);
@@ -249,7 +251,8 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
 template <int DT, int LP>
 static hipError_t launch_qknr_lp(const QkNormArgs& a, int u, hipStream_t s) {
     const void* fn = u == 1 ? (const void*)k_qknr<DT, LP, 1>
-                   : u == 2 ? (const void*)k_qknr<DT, LP, 2> : (const void*)k_qknr<DT, LP, 4>;
+                   : u == 2 ? (const void*)k_qknr<DT, LP, 2>
+                   : u == 3 ? (const void*)k_qknr<DT, LP, 3> : (const void*)k_qknr<DT, LP, 4>;
     QkNormArgs copy = a;
     void* args[] = {&copy};
     return hipLaunchKernel(fn, dim3((unsigned)a.T), dim3(256), args, 0, s);
@@ -267,12 +270,15 @@ static hipError_t launch_qknr_dt(const QkNormArgs& a, int lp, int u, hipStream_t
 }
 
 // U: passes of 256/LP heads; the caller guarantees NH * LP <= 4 * 256.
-hipError_t launch_qknr(const QkNormArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_qknr(const QkNormArgs& in, int dtype, hipStream_t s) {
+    QkNormArgs a = in;
+    a.inv_nq = 1.0 / ((double)a.Hq * a.D);
+    a.inv_nk = 1.0 / ((double)a.Hkv * a.D);
     int lp = 1;
     while (lp < a.D / 16) lp *= 2;
     const int NH = a.Hq + 2 * a.Hkv;
     const int passes = (NH * lp + 255) / 256;
-    const int u = passes <= 1 ? 1 : (passes <= 2 ? 2 : 4);
+    const int u = passes < 4 ? passes : 4;
     return dtype == DT_BF16 ? launch_qknr_dt<DT_BF16>(a, lp, u, s)
                             : launch_qknr_dt<DT_F16>(a, lp, u, s);
 }
