@@ -29,7 +29,26 @@ sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0
 T_BIG = 8192
-SPIN_CYCLES = 40_000_000     # host-side head start before a timed region
+# Lead-in before every timed region: ~35 ms of HBM-bound device copies on the
+# timed stream.  It gives the host a head start (the launches of the timed
+# region are enqueued while the copies run) and brings the GPU to its
+# sustained-load clocks.  Measured on MI355X: after an idle spin kernel the
+# first ~25 ms of memory-bound work run 6-15% slower than in steady state
+# (the activation kernel 86-94 us instead of 80-81 us), so an idle spin as
+# head start would time the clock ramp instead of the kernels.
+LEAD_COPIES = 100            # 1 GiB device copies (~0.33 ms each)
+_LEAD = {}
+
+
+def lead_in(torch, stream):
+    if "src" not in _LEAD:
+        _LEAD["src"] = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+        _LEAD["dst"] = torch.empty_like(_LEAD["src"])
+    with torch.cuda.stream(stream):
+        for _ in range(LEAD_COPIES):
+            _LEAD["dst"].copy_(_LEAD["src"])
+
+
 GROUP_REPEATS = 3
 EPS = 1e-6
 
@@ -211,12 +230,13 @@ def main():
 
         # ---- timed region 1: K steps in layer order ----------------------
         # Events only at the ends (an event record between kernels costs a
-        # few microseconds on this runtime).  A spin kernel first lets the
-        # host enqueue the whole region ahead of the GPU, so host-side launch
-        # cost opens no gaps (the spin itself is before the start event).
+        # few microseconds on this runtime).  The lead-in copies first let
+        # the host enqueue the whole region ahead of the GPU, so host-side
+        # launch cost opens no gaps, and bring the clocks to sustained load
+        # (the lead-in is before the start event).
         start, end = ev(), ev()
         torch.cuda.synchronize()
-        torch.cuda._sleep(SPIN_CYCLES)
+        lead_in(torch, stream)
         start.record(stream)
         for k in range(args.steps):
             for _, f in ops:
@@ -234,7 +254,7 @@ def main():
         reps = {name: [] for name, _ in ops}
         grouped = []
         for _ in range(GROUP_REPEATS):
-            torch.cuda._sleep(SPIN_CYCLES)
+            lead_in(torch, stream)
             marks = [ev() for _ in range(len(ops) + 1)]
             marks[0].record(stream)
             for j, (_, f) in enumerate(ops):
@@ -452,8 +472,8 @@ def run_gemm_act(torch, fr, workloads, dev, stream, reps=20, timed=True,
             del ws, w0
             continue
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):                  # spin on the same stream
-            torch.cuda._sleep(SPIN_CYCLES // 4)
+        with torch.cuda.stream(stream):                  # lead-in on the same stream
+            lead_in(torch, stream)
             e0.record(stream)
             for i in range(reps):
                 f(i)
@@ -528,11 +548,11 @@ def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
         if not timed:
             continue
         runs = []
-        with torch.cuda.stream(stream):                  # spin on the same stream
+        with torch.cuda.stream(stream):                  # lead-in on the same stream
             for _ in range(GROUP_REPEATS):
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
-                torch.cuda._sleep(SPIN_CYCLES)
+                lead_in(torch, stream)
                 e0.record(stream)
                 for i in range(reps):
                     f(i)
@@ -581,11 +601,11 @@ def run_qknorm(torch, fr, workloads, dev, stream, reps, timed=True, only=None):
         if not timed:
             continue
         runs = []
-        with torch.cuda.stream(stream):                  # spin on the same stream
+        with torch.cuda.stream(stream):                  # lead-in on the same stream
             for _ in range(GROUP_REPEATS):
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
-                torch.cuda._sleep(SPIN_CYCLES)
+                lead_in(torch, stream)
                 e0.record(stream)
                 for i in range(reps):
                     f(i)
