@@ -63,18 +63,19 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // Head group g of this wave: its chunks are loaded one group ahead of
-    // the group being processed.
+    // the group being processed.  Every lane loads (lanes past the row's
+    // heads or past D/16 re-read a valid chunk and store nothing): a load
+    // that some waves skip makes the compiler wait for every outstanding
+    // load, the prefetch included, before each group.
     const char* rowp = (const char*)a.qkv + t * (int64_t)NH * D * 2;
     const int off0 = j * 16;                 // bytes of chunk j, first half
     const int off1 = D + j * 16;             // bytes of chunk j, second half
-    auto load_group = [&](int g, u32x4& x0, u32x4& x1) {
-        x0 = x1 = (u32x4){0, 0, 0, 0};
-        const int head = (g0 + g) * HPW + hl;
-        if (g < ng && j < L && head < NH) {
-            const char* src = rowp + (int64_t)head * D * 2;
-            x0 = NT ? ld128_stream(src + off0) : ld128(src + off0);
-            x1 = NT ? ld128_stream(src + off1) : ld128(src + off1);
-        }
+    const int jc = min(j, L - 1);
+    auto load_group = [&](int g, u32x4& x0, u32x4& x1) {          // g < ng
+        const int head = min((g0 + g) * HPW + hl, NH - 1);
+        const char* src = rowp + (int64_t)head * D * 2 + jc * 16;
+        x0 = NT ? ld128_stream(src) : ld128(src);
+        x1 = NT ? ld128_stream(src + D) : ld128(src + D);
     };
     u32x4 n0, n1;
     load_group(0, n0, n1);
@@ -117,10 +118,7 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         for (int e = 0; e < 8; ++e) cs[e] = sn[e] = 0.0f;
     }
 
-#pragma unroll 1
-    for (int g = 0; g < ng; ++g) {                       // uniform trip count
-        const u32x4 c0 = n0, c1 = n1;
-        load_group(g + 1, n0, n1);
+    auto process = [&](int g, const u32x4 c0, const u32x4 c1) {
         const int head = (g0 + g) * HPW + hl;
         const bool active = (j < L) && (head < NH);
         const bool is_q = head < a.Hq;
@@ -153,6 +151,7 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         float ss = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) ss = fmaf(v[e], v[e], ss);
+        if (j >= L) ss = 0.0f;                           // padding lanes hold a re-read chunk
         ss = group_reduce<LP>(ss, OpSum());
         const bool has_norm = !is_v && (is_q ? a.qw : a.kw) != nullptr;
         if (has_norm) {
@@ -166,7 +165,7 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
                 v[8 + 2 * e + 1] = v[8 + 2 * e + 1] * rstd * hi16<DT>(w1[e]);
             }
         }
-        if (!active || is_v) continue;
+        if (!active || is_v) return;
 
         if (a.style == 0) {
 #pragma unroll
@@ -203,7 +202,7 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         if (is_q) {
             dst = (char*)a.q_out + ((t * a.Hq + head) * (int64_t)D) * 2;
         } else {
-            if (slot < 0) continue;
+            if (slot < 0) return;
             dst = (char*)a.kc + (slot * a.Hkv + (head - a.Hq)) * (int64_t)D * 2;
         }
         if constexpr (NTS) {
@@ -213,7 +212,15 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
             st128(dst + off0, o0);
             st128(dst + off1, o1);
         }
+    };
+
+#pragma unroll 1
+    for (int g = 0; g + 1 < ng; ++g) {                   // uniform trip count
+        const u32x4 c0 = n0, c1 = n1;
+        load_group(g + 1, n0, n1);
+        process(g, c0, c1);
     }
+    process(ng - 1, n0, n1);
 }
 
 template <int DT, bool NT>
