@@ -227,12 +227,50 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
         return;
     }
 
+    // Pass 2 of the plain modes, before the row reduction: t = ro * W
+    // (a float pair for the (1+w) case) and max |t|, which does not depend
+    // on rstd, so the per-token amax travels with the sum of squares and the
+    // row needs one cross-wave step, not two.
+    float th[CPL][8], tl[CPL][8];
+    float tmax = 0.0f;
+    if constexpr (!ADA) {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const u32 rw = rv[k][e >> 1];
+                const float ro = (e & 1) ? hi16<DT>(rw) : lo16<DT>(rw);
+                float hi = ro, lo = 0.0f;
+                if constexpr (MODE == M_MUL) {
+                    const u32 ww = wv[k][e >> 1];
+                    hi = ro * ((e & 1) ? hi16<DT>(ww) : lo16<DT>(ww));     // exact
+                } else if constexpr (MODE == M_ONE_PLUS) {
+                    const u32 ww = wv[k][e >> 1];
+                    const float c = 1.0f + ((e & 1) ? hi16<DT>(ww) : lo16<DT>(ww));
+                    hi = ro * c;
+                    lo = fmaf(ro, c, -hi);                                  // exact remainder
+                }
+                th[k][e] = hi;
+                tl[k][e] = lo;
+                if (ok[k]) tmax = fmaxf(tmax, fabsf(hi));
+            }
+        }
+    }
+    const bool token_max = !ADA && !MX && a.qmode == 1;
     double ss = wave_sum_d(ss0 + ss1);
+    if (token_max) tmax = wave_reduce(tmax, OpMax());
     if (a.nw > 1) {
-        if (lane == 0) red_ss[wave] = ss;
+        if (lane == 0) {
+            red_ss[wave] = ss;
+            red_max[wave] = tmax;
+        }
         __syncthreads();
         ss = red_ss[rw * a.nw];
         for (int w = 1; w < a.nw; ++w) ss += red_ss[rw * a.nw + w];
+        if (token_max) {
+            tmax = red_max[rw * a.nw];
+            for (int w = 1; w < a.nw; ++w) tmax = fmaxf(tmax, red_max[rw * a.nw + w]);
+        }
     }
     const double rstd_d = 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
 
@@ -276,30 +314,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
             st_out<NTS>(orow + (k * stride + ww * 64 + lane) * 8, q);
         }
     } else {
-        // Pass 2 (plain): t = ro * W (float pair for the (1+w) case).
-        float th[CPL][8], tl[CPL][8];
-        float tmax = 0.0f;
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const u32 rw = rv[k][e >> 1];
-                const float ro = (e & 1) ? hi16<DT>(rw) : lo16<DT>(rw);
-                float hi = ro, lo = 0.0f;
-                if constexpr (MODE == M_MUL) {
-                    const u32 ww = wv[k][e >> 1];
-                    hi = ro * ((e & 1) ? hi16<DT>(ww) : lo16<DT>(ww));     // exact
-                } else if constexpr (MODE == M_ONE_PLUS) {
-                    const u32 ww = wv[k][e >> 1];
-                    const float c = 1.0f + ((e & 1) ? hi16<DT>(ww) : lo16<DT>(ww));
-                    hi = ro * c;
-                    lo = fmaf(ro, c, -hi);                                  // exact remainder
-                }
-                th[k][e] = hi;
-                tl[k][e] = lo;
-                if (ok[k]) tmax = fmaxf(tmax, fabsf(hi));
-            }
-        }
+        // Pass 3 (plain): the FP8 / FP4 codes of t * rstd * K.
         if constexpr (MX) {
             const float Kh = (float)rstd_d;
             const float Kl = (float)(rstd_d - (double)Kh);
@@ -333,13 +348,6 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
         }
         double K = rstd_d * (double)a.static_scale;
         if (a.qmode == 1) {
-            tmax = wave_reduce(tmax, OpMax());
-            if (a.nw > 1) {
-                if (lane == 0) red_max[wave] = tmax;
-                __syncthreads();
-                tmax = red_max[rw * a.nw];
-                for (int w = 1; w < a.nw; ++w) tmax = fmaxf(tmax, red_max[rw * a.nw + w]);
-            }
             const double amax = fmax((double)tmax * rstd_d, (double)1e-10f);
             const float s = (float)(amax / 448.0);
             K = rstd_d / (double)s;
@@ -369,12 +377,15 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
 
 template <int DT, int MODE, bool NT, bool MX>
 static hipError_t launch_norm_mode(const NormArgs& a, int cpl, hipStream_t s) {
+    // the adaptive op's outputs are stored cacheable even when streaming
+    // (measured 2-3% faster at 8192 x 1024 fp16)
+    constexpr bool NTS = NT && MODE != M_ADA;
     const void* fn;
     switch (cpl) {
-    case 1: fn = (const void*)k_norm<DT, 1, MODE, NT, NT, MX>; break;
-    case 2: fn = (const void*)k_norm<DT, 2, MODE, NT, NT, MX>; break;
-    case 4: fn = (const void*)k_norm<DT, 4, MODE, NT, NT, MX>; break;
-    default: fn = (const void*)k_norm<DT, 8, MODE, NT, NT, MX>; break;
+    case 1: fn = (const void*)k_norm<DT, 1, MODE, NT, NTS, MX>; break;
+    case 2: fn = (const void*)k_norm<DT, 2, MODE, NT, NTS, MX>; break;
+    case 4: fn = (const void*)k_norm<DT, 4, MODE, NT, NTS, MX>; break;
+    default: fn = (const void*)k_norm<DT, 8, MODE, NT, NTS, MX>; break;
     }
     NormArgs copy = a;
     void* args[] = {&copy};
@@ -409,11 +420,12 @@ struct NormShape {
 // Launch shape: at most two 16-byte chunks per lane, so a row spreads over
 // up to 8 wavefronts (more chunks per lane only for rows wider than 8192
 // values), and in the bandwidth regime (T >= 2048) two single-wave rows per
-// workgroup and non-temporal streaming.  Measured on MI355X at T = 8192:
-// H = 4096 bf16 runs at ~75% of 8 TB/s with 4 waves x 2 chunks per row
-// (one wave x 8 chunks: 65%; without non-temporal access: 50%); H = 1024
-// fp16 adaptive at ~77% with 2 rows per workgroup.  Small batches keep the
-// outputs cacheable for the next op.
+// workgroup and non-temporal streaming.  Measured on MI355X at T = 8192 in
+// steady state: H = 4096 bf16 at ~70% of 8 TB/s with 4 waves x 2 chunks per
+// row (2 waves x 4 chunks: 69%; 1 wave x 8 chunks: 65%; 8 waves x 1 chunk:
+// 54%; cacheable stores: 64%); H = 1024 fp16 adaptive at ~69% with 2 rows
+// per workgroup (1 or 4 rows: 65-67%).  Small batches keep the outputs
+// cacheable for the next op.
 static NormShape pick_norm_shape(int64_t T, int H, bool adaptive) {
     (void)adaptive;
     const int C = H / 8;
