@@ -32,7 +32,7 @@ KERNELS = {  # kernel name prefix -> (op, algorithmic read bytes, write bytes)
     "void fr::k_norm<1, 2, 1, true, true, false>": (
         "resid_rmsnorm_fp8 T=8192 H=4096 bf16 MUL TOKEN",
         8192 * 4096 * 4 + 4096 * 2, 8192 * 4096 * 3 + 8192 * 4),
-    "void fr::k_norm<0, 2, 3, true, true, false>": (
+    "void fr::k_norm<0, 2, 3, true, false, false>": (
         "adarms_gate_res_fp8 T=8192 H=1024 f16 STATIC",
         8192 * 1024 * 10, 8192 * 1024 * 3),
     "void fr::k_qkv<1, 8, true": (
