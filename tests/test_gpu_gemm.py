@@ -157,6 +157,31 @@ def test_gemm_gated_act(fr, case):
     announce(f"  fp8 identical {ident:.6f}, scale max rel err {rel:.2e}")
 
 
+def test_gemm_bench_shapes(fr):
+    """The two larger shapes the benchmark times, in its launch configuration:
+    1024 x 2048 x 6144 in full, 4096 x 4096 x 12288 on 16 sampled rows (rows
+    are independent, so the oracle runs on those rows only)."""
+    announce("gemm_gated_act bench shape M=1024 K=2048 I=6144")
+    inp = workloads.gemm_inputs(1024, 2048, 6144, 1824)
+    q_g, s_g = run_gemm(fr, inp, oracle.ACT_SWIGLU)
+    q_o, s_o, _ = oracle.gemm_gated_act_fp8(inp["a"], inp["a_scales"], inp["w"],
+                                            inp["w_scales"], oracle.ACT_SWIGLU)
+    check_gemm_interval(q_g, s_g, q_o, s_o, inp, oracle.ACT_SWIGLU)
+
+    M, K, I = 4096, 4096, 12288
+    announce(f"gemm_gated_act bench shape M={M} K={K} I={I}, 16 sampled rows")
+    inp = workloads.gemm_inputs(M, K, I, 4896)
+    q_g, s_g = run_gemm(fr, inp, oracle.ACT_SWIGLU)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 2047, M - 2, M - 1],
+                                     np.random.default_rng(4896).integers(0, M, 9)]))
+    sub = {"a": inp["a"][rows], "a_scales": inp["a_scales"][rows],
+           "w": inp["w"], "w_scales": inp["w_scales"]}
+    q_o, s_o, _ = oracle.gemm_gated_act_fp8(sub["a"], sub["a_scales"], sub["w"],
+                                            sub["w_scales"], oracle.ACT_SWIGLU)
+    ident, rel = check_gemm_interval(q_g[rows], s_g[rows], q_o, s_o, sub, oracle.ACT_SWIGLU)
+    announce(f"  sampled rows {len(rows)}: fp8 identical {ident:.6f}, scale max rel err {rel:.2e}")
+
+
 def test_gemm_worked_example(fr):
     announce("gemm worked example")
     K, I = 128, 128
