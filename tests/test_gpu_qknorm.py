@@ -30,6 +30,7 @@ CASES = [
     ("d256_layer_head", 10, 8, 1, 256, F16, 2, False, False, None, 0, 1e4, 1.0, 606),
     ("d16_rms_full", 9, 3, 3, 16, BF16, 1, True, False, None, 1, 1e4, 1.0, 607),
     ("wan_bench_8192", 8192, 40, 40, 128, BF16, 1, True, True, (22, 21, 21), 1, 1e4, 1.0, 608),
+    ("chameleon_bench_8192", 8192, 32, 32, 128, BF16, 2, False, False, None, 0, 1e4, 1.0, 609),
 ]
 
 
