@@ -18,15 +18,18 @@
 // reduction plus one permlane16 swap.  The scale is the correctly rounded
 // amax / 448 (fma-corrected quotient); |h / scale| <= 448 (1 + 3 ulp) < 464,
 // so the e4m3 conversion never sees a value that would overflow and needs no
-// clamp.  (Measured on MI355X at 8192 x 12288: this layout with 4 waves per
-// workgroup is 5-15% faster than 2 or 8 waves per workgroup or 32-byte
-// lane-contiguous chunks.)
+// clamp.  The wave's codes form one contiguous span (STEPS * 256 bytes);
+// they are gathered in LDS and leave as 16-byte stores (4-byte stores straight
+// from each step: 3% slower).  (Measured on MI355X at 8192 x 12288: this
+// layout with 4 waves per workgroup is 5-15% faster than 2 or 8 waves per
+// workgroup or 32-byte lane-contiguous chunks.)
 //
 // MX FP4 output (Hy-Embodied report, 04 step 9 and 06: the SwiGLU FP4
 // producer): the same loads and activation; a block of 32 outputs is 8
 // consecutive lanes, its maximum a DPP reduction over 8 lanes, whose fp32
 // exponent gives the E8M0 code; the 4 outputs of a lane become 16 bits of
-// E2M1 codes after an exact power-of-two scaling.
+// E2M1 codes after an exact power-of-two scaling; codes and E8M0 scales are
+// gathered in LDS like the FP8 codes.
 #include "fr_device.h"
 #include "fr_launch.h"
 
@@ -39,6 +42,12 @@ constexpr int kActSteps = 8;   // block pairs per wave (bandwidth regime)
 template <int DT, int ACT, int STEPS = kActSteps, bool NTL = true, bool NTS = true,
           bool MX = false>
 __global__ __launch_bounds__(256) void k_act(ActArgs a) {
+    // the wave's codes (STEPS block pairs = one contiguous span: FP8 STEPS *
+    // 256 bytes; MX FP4 STEPS * 128 bytes, then its STEPS * 8 E8M0 codes),
+    // gathered so they leave as 16-byte stores
+    constexpr int SPAN = MX ? STEPS * 136 : STEPS * 256;
+    __shared__ __attribute__((aligned(16))) uint8_t obuf[4][SPAN];
+    uint8_t* ob = obuf[threadIdx.x >> 6];
     const int lane = threadIdx.x & 63;
     const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (wid >= a.waves) return;                          // whole wave exits
@@ -52,11 +61,9 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
     float* srow = a.scales + t * (int64_t)a.nb;
 
     u32x4 in[STEPS];                                     // all loads first
-    int blk[STEPS];
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
         const int b = (wc * STEPS + k) * 2 + half;
-        blk[k] = b;
         const unsigned off = (unsigned)(b < a.nb ? b : a.nb - 1) * 512u + (unsigned)cb * 16u;
         in[k] = NTL ? ld128_stream(row + off) : ld128(row + off);
     }
@@ -75,15 +82,8 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
             m = group_reduce<8>(m, OpMax());             // block of 32 outputs
             const int code = mx_code(m);
             const u32 p = pack_e2m1x4(h[0], h[1], h[2], h[3], mx_mult(code));
-            const int b = blk[k];
-            if (b < a.nb) {
-                uint16_t* dst = (uint16_t*)(a.out + t * (int64_t)(a.I >> 1) +
-                                            (unsigned)b * 64u + (unsigned)cb * 2u);
-                if constexpr (NTS) __builtin_nontemporal_store((uint16_t)p, dst);
-                else *dst = (uint16_t)p;
-                if ((cb & 7) == 0)
-                    a.mx_scales[t * (int64_t)(a.I >> 5) + b * 4 + (cb >> 3)] = (uint8_t)code;
-            }
+            *reinterpret_cast<uint16_t*>(ob + (2 * k + half) * 64 + cb * 2) = (uint16_t)p;
+            if ((cb & 7) == 0) ob[STEPS * 128 + (2 * k + half) * 4 + (cb >> 3)] = (uint8_t)code;
             continue;
         }
         // Block maximum over 32 lanes (all 64 lanes take part).
@@ -91,12 +91,10 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
         m = rows_pair(m, OpMax());
         const float s = div448(fmaxf(m, 1e-10f));        // correctly rounded
         const float inv = __builtin_amdgcn_rcpf(s);
-        const int b = blk[k];
-        if (b < a.nb) {
+        {
             int q = __builtin_amdgcn_cvt_pk_fp8_f32(h[0] * inv, h[1] * inv, 0, false);
             q = __builtin_amdgcn_cvt_pk_fp8_f32(h[2] * inv, h[3] * inv, q, true);
-            u32* dst = (u32*)(orow + (unsigned)b * 128u + (unsigned)cb * 4u);
-            if constexpr (NTS) __builtin_nontemporal_store((u32)q, dst); else *dst = (u32)q;
+            *reinterpret_cast<u32*>(ob + (2 * k + half) * 128 + cb * 4) = (u32)q;
         }
         // gather the two block scales of this step into lanes 2k and 2k+1
         const int si = __builtin_bit_cast(int, s);
@@ -104,9 +102,37 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
         const float s_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(si, 32));
         sc = lane == 2 * k ? s_lo : (lane == 2 * k + 1 ? s_hi : sc);
     }
-    if constexpr (MX) return;
-    // one contiguous store of the wave's 2 * STEPS block scales
     const int b0 = wc * STEPS * 2;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (MX) {
+        // codes: 16-byte chunk c is in block b0 + c / 4; E8M0 codes: 4 per block
+        uint8_t* o4 = a.out + t * (int64_t)(a.I >> 1) + (int64_t)b0 * 64;
+#pragma unroll
+        for (int c = lane; c < STEPS * 8; c += 64) {
+            if (b0 + (c >> 2) < a.nb) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(ob + c * 16);
+                if constexpr (NTS) st128_stream(o4 + c * 16, v); else st128(o4 + c * 16, v);
+            }
+        }
+        if (lane < 2 * STEPS && b0 + lane < a.nb) {
+            const u32 e = *reinterpret_cast<const u32*>(ob + STEPS * 128 + lane * 4);
+            u32* dst = reinterpret_cast<u32*>(a.mx_scales + t * (int64_t)(a.I >> 5) + (b0 + lane) * 4);
+            if constexpr (NTS) __builtin_nontemporal_store(e, dst); else *dst = e;
+        }
+        return;
+    }
+    // the codes: 16-byte chunk c of the wave's span is block b0 + c / 8
+#pragma unroll
+    for (int c = lane; c < STEPS * 16; c += 64) {
+        if (b0 + (c >> 3) < a.nb) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ob + c * 16);
+            if constexpr (NTS) st128_stream(orow + (int64_t)b0 * 128 + c * 16, v);
+            else st128(orow + (int64_t)b0 * 128 + c * 16, v);
+        }
+    }
+    // one contiguous store of the wave's 2 * STEPS block scales
     if (lane < 2 * STEPS && b0 + lane < a.nb) {
         if constexpr (NTS) __builtin_nontemporal_store(sc, srow + b0 + lane); else srow[b0 + lane] = sc;
     }
