@@ -157,8 +157,8 @@ static hipError_t launch_act_cfg(const ActArgs& in, int act, hipStream_t s) {
 
 // Bandwidth regime (T >= 2048): 8 block pairs per wave, non-temporal loads,
 // cacheable stores.  Measured back to back on MI355X at 8192 x 12288 bf16
-// (~6.1 TB/s): 4 pairs with non-temporal stores ~3-6% slower, cacheable loads
-// ~15% slower.  Small batches: 2 block pairs per wave for more parallel waves,
+// (~6.3 TB/s): 4, 6 or 12 pairs 1-5% slower, non-temporal stores ~5% slower,
+// cacheable loads ~15% slower.  Small batches: 2 block pairs per wave for more parallel waves,
 // everything cacheable for the next op.
 template <bool MX>
 static hipError_t launch_act_fmt(const ActArgs& a, int dtype, int act, hipStream_t s) {
