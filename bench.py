@@ -16,7 +16,6 @@ timed on a bounded sample of the same workload.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -74,8 +73,8 @@ def op_bytes():
 
 
 def kernel_source_hash(name):
-    with open(os.path.join(HERE, "memory_bound_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    from bench_profile import code_hash
+    return code_hash(os.path.join(HERE, "memory_bound_amd", "csrc", name))
 
 
 def load_traffic(kernel_file, per_launch_bytes_key):
@@ -86,7 +85,7 @@ def load_traffic(kernel_file, per_launch_bytes_key):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_sha256_16") != kernel_source_hash(kernel_file):
+    if d.get("code_sha256_16") != kernel_source_hash(kernel_file):
         return None
     return d.get(per_launch_bytes_key)
 

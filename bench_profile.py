@@ -21,6 +21,7 @@ import collections
 import hashlib
 import json
 import os
+import re
 import sqlite3
 import sys
 
@@ -58,6 +59,18 @@ KERNELS = {  # kernel name prefix -> (op, algorithmic read bytes, write bytes)
         12288 * 2048 + 128 * 2048 + 128 * 16 * 4 + 96 * 16 * 4,
         128 * 6144 + 128 * 48 * 4),
 }
+
+
+def code_hash(path):
+    """sha256 (16 hex digits) of a C++ source with its comments and blank
+    space removed: a counter record stays valid across comment edits and
+    becomes stale on any change to the code itself."""
+    with open(path) as fh:
+        src = fh.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def per_kernel(db):
@@ -131,10 +144,9 @@ def pmc(fetch_db, write_db):
     print("\n".join(lines))
     dom = out.get(ACT_FP8)
     if dom:
-        with open(os.path.join(HERE, "memory_bound_amd", "csrc", "fr_act.hip"), "rb") as fh:
-            sha = hashlib.sha256(fh.read()).hexdigest()[:16]
+        sha = code_hash(os.path.join(HERE, "memory_bound_amd", "csrc", "fr_act.hip"))
         rec = {"kernel": "fr::k_act<bf16, SwiGLU>", "workload": "T=8192 I=12288 bf16",
-               "source_sha256_16": sha,
+               "code_sha256_16": sha,
                "hbm_bytes_per_launch": round(dom["read_bytes"] + dom["write_bytes"]),
                "read_bytes_per_launch": round(dom["read_bytes"]),
                "write_bytes_per_launch": round(dom["write_bytes"]),
