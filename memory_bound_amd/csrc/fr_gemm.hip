@@ -278,13 +278,16 @@ static hipError_t launch_gemm_cfg(const GemmActArgs& in, int act, hipStream_t s)
 }
 
 // Row groups per tile.  Measured on MI355X (hidden 2048 / 4096, inter 6144 /
-// 12288, 128 to 4096 tokens): 64-row tiles win once they still give every CU
-// a tile, 32-row tiles otherwise; 128-row tiles and 4 K blocks in flight
-// were never faster.
+// 12288, 128 to 4096 tokens): 64-row tiles win once they still give three
+// quarters of the 256 CUs a tile (128 x 4096 x 12288: 192 tiles, 41.7 us vs
+// 47.1 us with 32-row tiles), 32-row tiles otherwise (128 x 2048 x 6144: 96
+// vs 192 tiles, 26.1 vs 19.1 us); 128-row tiles, 4 K blocks in flight, and
+// waves loading their own activation fragments (no LDS stage) were never
+// faster.
 hipError_t launch_gemm_act(const GemmActArgs& in, int act, hipStream_t s) {
     const int64_t nt = in.I / 128;
     const int KB = in.K / 128;
-    if (64 * KB <= kGemmPanel && ((int64_t)in.M + 63) / 64 * nt >= 256)
+    if (64 * KB <= kGemmPanel && ((int64_t)in.M + 63) / 64 * nt >= 192)
         return launch_gemm_cfg<2, 2>(in, act, s);
     return launch_gemm_cfg<1, 2>(in, act, s);
 }
