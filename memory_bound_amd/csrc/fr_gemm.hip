@@ -41,7 +41,10 @@
 // pair swap gives both lanes act(g) * u.  Row maxima are reduced across
 // the wave's 32 outputs with DPP, combined across the 4 waves in LDS, and
 // the codes go through LDS so each output row leaves as 128 contiguous
-// bytes.  Tiles are ordered so that each XCD (which serves blocks b with
+// bytes; the row scales are gathered in LDS and leave as one store.  Lanes
+// that hold the same value (a gate/up pair, a reduced half-wave) all write
+// it, so the epilogue has no per-row branches (it was ~20% of the kernel at
+// 128 tokens with them).  Tiles are ordered so that each XCD (which serves blocks b with
 // b % 8 fixed) walks a contiguous range of tiles: the row tiles of one
 // 256-column weight panel run together on one XCD and share its L2.
 #include "fr_device.h"
@@ -88,6 +91,7 @@ __global__ __launch_bounds__(256) void k_gemm_act(GemmActArgs a) {
     __shared__ __attribute__((aligned(16))) float asp[kGemmPanel];          // [kb][row]
     __shared__ __attribute__((aligned(16))) float bsp[2 * kGemmMaxKB];     // [block][kb]
     __shared__ __attribute__((aligned(16))) float red[ROWS * 4];           // [row][wave]
+    __shared__ __attribute__((aligned(16))) float osc[ROWS];               // row scales
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;                      // column quarter
@@ -220,7 +224,8 @@ __global__ __launch_bounds__(256) void k_gemm_act(GemmActArgs a) {
                 float m = fmaxf(fabsf(acc[g][0][r]), fabsf(acc[g][1][r]));
                 m = group_reduce<16>(m, OpMax());
                 m = rows_pair(m, OpMax());               // over the 32 lanes of kh
-                if (rl == 0) red[(32 * g + 8 * (r >> 2) + 4 * kh + (r & 3)) * 4 + w] = m;
+                // every lane of the half holds m: all write it (no branch)
+                red[(32 * g + 8 * (r >> 2) + 4 * kh + (r & 3)) * 4 + w] = m;
             }
         }
     }
@@ -240,16 +245,18 @@ __global__ __launch_bounds__(256) void k_gemm_act(GemmActArgs a) {
                 // |h * inv| <= 448 (1 + 3 ulp) < 464: no clamp needed
                 const int q = __builtin_amdgcn_cvt_pk_fp8_f32(acc[g][0][r] * inv,
                                                               acc[g][1][r] * inv, 0, false);
-                if (!(rl & 1)) {
-                    otile[row * 128 + 32 * w + (rl >> 1)] = (uint8_t)q;
-                    otile[row * 128 + 32 * w + 16 + (rl >> 1)] = (uint8_t)(q >> 8);
-                }
-                if (w == 0 && rl == 0 && m0 + row < a.M)
-                    a.out_scales[(int64_t)(m0 + row) * nbo + n_tile] = s;
+                // the two lanes of a gate/up pair hold the same codes and
+                // the 32 lanes of a half the same scale: duplicate writes of
+                // equal values instead of branches
+                otile[row * 128 + 32 * w + (rl >> 1)] = (uint8_t)q;
+                otile[row * 128 + 32 * w + 16 + (rl >> 1)] = (uint8_t)(q >> 8);
+                osc[row] = s;
             }
         }
     }
     __syncthreads();
+    if (threadIdx.x < ROWS && m0 + (int)threadIdx.x < a.M)   // one store per row
+        a.out_scales[(int64_t)(m0 + threadIdx.x) * nbo + n_tile] = osc[threadIdx.x];
     {
 #pragma unroll
         for (int i = 0; i < RG; ++i) {
