@@ -30,6 +30,7 @@ struct NormArgs {
     int qmode;
     float eps;
     float static_scale;
+    double inv_h;           // 1 / H: set by launch_norm
 };
 
 // Packed QKV split + per-head norm + RoPE + paged KV write.

@@ -44,6 +44,31 @@ namespace fr {
 
 enum { M_NONE = 0, M_MUL = 1, M_ONE_PLUS = 2, M_ADA = 3, M_LAYER = 4 };
 
+// Per-row fp64 scalars without the runtime's division and square-root
+// sequences: the hardware estimates refined by two Newton steps each
+// (an estimate good to ~2^-22 becomes good to the last bits of fp64), and
+// the quotient by 448 as a product with one remainder correction.
+__device__ __forceinline__ double rsqrt_d(double x) {         // x > 0
+    double y = __builtin_amdgcn_rsq(x);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const double e = fma(-(x * y), y, 1.0);               // 1 - x y^2
+        y = fma(0.5 * y, e, y);
+    }
+    return y;
+}
+__device__ __forceinline__ double rcp_d(double x) {           // x > 0
+    double r = __builtin_amdgcn_rcp(x);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r = fma(r, fma(-x, r, 1.0), r);
+    return r;
+}
+__device__ __forceinline__ double div448_d(double v) {
+    constexpr double kInv = 1.0 / 448.0;
+    const double q0 = v * kInv;
+    return fma(fma(-q0, 448.0, v), kInv, q0);
+}
+
 template <bool NT>
 __device__ __forceinline__ u32x4 ld_in(const void* p) {
     if constexpr (NT) return ld128_stream(p); else return ld128(p);
@@ -155,7 +180,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
             for (int e = 0; e < 4; ++e)
                 s1 += (double)lo16<DT>(rv[k][e]) + (double)hi16<DT>(rv[k][e]);
         }
-        const double mean_d = row_sum(s1, red_ss) / (double)a.H;
+        const double mean_d = row_sum(s1, red_ss) * a.inv_h;
         double s2 = 0.0;
 #pragma unroll
         for (int k = 0; k < CPL; ++k) {
@@ -167,8 +192,8 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
                 s2 = fma(d0, d0, fma(d1, d1, s2));
             }
         }
-        const double var_d = row_sum(s2, red_ss2) / (double)a.H;
-        const float rstd = (float)(1.0 / sqrt(var_d + (double)a.eps));
+        const double var_d = row_sum(s2, red_ss2) * a.inv_h;
+        const float rstd = (float)rsqrt_d(var_d + (double)a.eps);
         const float mean = (float)mean_d;
         float y[CPL][8];
         float amax = 0.0f;
@@ -212,7 +237,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
                 amax = red_max[rw * a.nw];
                 for (int w = 1; w < a.nw; ++w) amax = fmaxf(amax, red_max[rw * a.nw + w]);
             }
-            const float s = (float)((double)fmaxf(amax, 1e-10f) / 448.0);
+            const float s = div448(fmaxf(amax, 1e-10f));     // correctly rounded
             mult = 1.0f / s;
             if (row_ok && ww == 0 && lane == 0) a.scales[t] = s;
         }
@@ -272,7 +297,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
             for (int w = 1; w < a.nw; ++w) tmax = fmaxf(tmax, red_max[rw * a.nw + w]);
         }
     }
-    const double rstd_d = 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
+    const double rstd_d = rsqrt_d(ss * a.inv_h + (double)a.eps);
 
     if constexpr (ADA) {
         // Pass 2 (adaptive): y = n * (1 + scale) + shift in fp32.
@@ -301,7 +326,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
                 amax = red_max[rw * a.nw];
                 for (int w = 1; w < a.nw; ++w) amax = fmaxf(amax, red_max[rw * a.nw + w]);
             }
-            const float s = (float)((double)fmaxf(amax, 1e-10f) / 448.0);
+            const float s = div448(fmaxf(amax, 1e-10f));     // correctly rounded
             mult = 1.0f / s;
             if (row_ok && ww == 0 && lane == 0) a.scales[t] = s;
         }
@@ -349,8 +374,8 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
         double K = rstd_d * (double)a.static_scale;
         if (a.qmode == 1) {
             const double amax = fmax((double)tmax * rstd_d, (double)1e-10f);
-            const float s = (float)(amax / 448.0);
-            K = rstd_d / (double)s;
+            const float s = (float)div448_d(amax);
+            K = rstd_d * rcp_d((double)s);
             if (row_ok && ww == 0 && lane == 0) a.scales[t] = s;
         }
         const float Kh = (float)K;
@@ -447,6 +472,7 @@ hipError_t launch_norm(const NormArgs& in, int dtype, int kind, hipStream_t s) {
     const bool layer = kind == NORM_LAYER_FP8 || kind == NORM_LAYER_MXFP4;
     const bool mx = kind == NORM_MXFP4 || kind == NORM_LAYER_MXFP4;
     const NormShape sh = pick_norm_shape(a.T, a.H, adaptive);
+    a.inv_h = 1.0 / (double)a.H;
     a.nw = sh.nw;
     a.rpb = sh.rpb;
     const int mode = adaptive ? M_ADA : (layer ? M_LAYER : a.wmode);
