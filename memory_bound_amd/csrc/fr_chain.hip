@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void k_chain(ChainArgs a) {
                 }
             }
             ss = wave_sum_d(ss);
-            const float rstd = (float)(1.0 / sqrt(ss / (double)H + (double)a.eps));
+            const float rstd = (float)rsqrt_d(ss * (1.0 / (double)H) + (double)a.eps);
             const float mult = a.static_scale;
             uint8_t* orow = a.out + (int64_t)n * T * H + (int64_t)t * H;
 #pragma unroll

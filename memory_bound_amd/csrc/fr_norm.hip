@@ -44,31 +44,6 @@ namespace fr {
 
 enum { M_NONE = 0, M_MUL = 1, M_ONE_PLUS = 2, M_ADA = 3, M_LAYER = 4 };
 
-// Per-row fp64 scalars without the runtime's division and square-root
-// sequences: the hardware estimates refined by two Newton steps each
-// (an estimate good to ~2^-22 becomes good to the last bits of fp64), and
-// the quotient by 448 as a product with one remainder correction.
-__device__ __forceinline__ double rsqrt_d(double x) {         // x > 0
-    double y = __builtin_amdgcn_rsq(x);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const double e = fma(-(x * y), y, 1.0);               // 1 - x y^2
-        y = fma(0.5 * y, e, y);
-    }
-    return y;
-}
-__device__ __forceinline__ double rcp_d(double x) {           // x > 0
-    double r = __builtin_amdgcn_rcp(x);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) r = fma(r, fma(-x, r, 1.0), r);
-    return r;
-}
-__device__ __forceinline__ double div448_d(double v) {
-    constexpr double kInv = 1.0 / 448.0;
-    const double q0 = v * kInv;
-    return fma(fma(-q0, 448.0, v), kInv, q0);
-}
-
 template <bool NT>
 __device__ __forceinline__ u32x4 ld_in(const void* p) {
     if constexpr (NT) return ld128_stream(p); else return ld128(p);
