@@ -114,7 +114,8 @@ __device__ __forceinline__ double dpp_d(double v) {
     return __builtin_bit_cast(double, w);
 }
 
-enum { DPP_PAIR = 0xB1, DPP_QUAD = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140 };
+enum { DPP_PAIR = 0xB1, DPP_QUAD = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140,
+       DPP_ROR2 = 0x122, DPP_ROR4 = 0x124, DPP_ROR8 = 0x128 };   // rotations in a row
 
 struct OpSum {
     __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }

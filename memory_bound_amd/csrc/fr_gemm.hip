@@ -37,9 +37,10 @@
 // MI355X, this layout runs 1.5x (128 tokens) to 3x (4096 tokens) faster
 // than fragments loaded straight from the row-major weight.
 //
-// Epilogue: a gate column and its up partner sit in adjacent lanes; a DPP
-// pair swap gives both lanes act(g) * u.  Row maxima are reduced across
-// the wave's 32 outputs with DPP, combined across the 4 waves in LDS, and
+// Epilogue: a gate column and its up partner sit in adjacent lanes; the
+// pair splits the rows, each lane evaluating act(g) * u for half of them
+// after one DPP pair swap.  Row maxima are reduced across the wave's 32
+// outputs with DPP, combined across the 4 waves in LDS, and
 // the codes go through LDS so each output row leaves as 128 contiguous
 // bytes; the row scales are gathered in LDS and leave as one store.  Lanes
 // that hold the same value (a gate/up pair, a reduced half-wave) all write
@@ -205,26 +206,38 @@ __global__ __launch_bounds__(256) void k_gemm_act(GemmActArgs a) {
     }
 
     // Epilogue.  Column 64w + 32t + rl of the tile is gate (rl even) or up
-    // (rl odd) of output 32w + 16t + rl/2 of the block.
+    // (rl odd) of output 32w + 16t + rl/2 of the block.  The two lanes of a
+    // gate/up pair split the accumulator registers: lane parity p = rl & 1
+    // takes r = 2k + p (k < 8), gets its partner's half of each pair with
+    // one DPP pair swap, and evaluates act(g) * u once per output.  Row
+    // maxima are then reduced over the 16 lanes of parity p in the half
+    // (DPP rotations by 2, 4, 8 within a row, then the row swap).
+    const int p = rl & 1;
+    float h[RG][2][8];
     {
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float v = acc[g][t][r];
-                    const float pv = dpp_f<DPP_PAIR>(v);
-                    const float gv = (rl & 1) ? pv : v, uv = (rl & 1) ? v : pv;
-                    acc[g][t][r] = gate_act<ACT>(gv) * uv;
+                for (int k = 0; k < 8; ++k) {
+                    const float a0 = acc[g][t][2 * k], a1 = acc[g][t][2 * k + 1];
+                    const float send = p ? a0 : a1;      // what the partner needs
+                    const float own = p ? a1 : a0;       // register r = 2k + p
+                    const float recv = dpp_f<DPP_PAIR>(send);
+                    const float gv = p ? recv : own, uv = p ? own : recv;
+                    h[g][t][k] = gate_act<ACT>(gv) * uv;
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float m = fmaxf(fabsf(acc[g][0][r]), fabsf(acc[g][1][r]));
-                m = group_reduce<16>(m, OpMax());
-                m = rows_pair(m, OpMax());               // over the 32 lanes of kh
-                // every lane of the half holds m: all write it (no branch)
+            for (int k = 0; k < 8; ++k) {
+                float m = fmaxf(fabsf(h[g][0][k]), fabsf(h[g][1][k]));
+                m = fmaxf(m, dpp_f<DPP_ROR2>(m));
+                m = fmaxf(m, dpp_f<DPP_ROR4>(m));
+                m = fmaxf(m, dpp_f<DPP_ROR8>(m));
+                m = rows_pair(m, OpMax());               // 16 lanes of parity p
+                const int r = 2 * k + p;
+                // the 16 lanes of the class hold m: all write it (no branch)
                 red[(32 * g + 8 * (r >> 2) + 4 * kh + (r & 3)) * 4 + w] = m;
             }
         }
@@ -236,18 +249,18 @@ __global__ __launch_bounds__(256) void k_gemm_act(GemmActArgs a) {
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int k = 0; k < 8; ++k) {
+                const int r = 2 * k + p;
                 const int row = 32 * g + 8 * (r >> 2) + 4 * kh + (r & 3);
                 const float4 mm = *reinterpret_cast<const float4*>(red + row * 4);
                 const float mx = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
                 const float s = div448(fmaxf(mx, 1e-10f));   // correctly rounded
                 const float inv = __builtin_amdgcn_rcpf(s);
                 // |h * inv| <= 448 (1 + 3 ulp) < 464: no clamp needed
-                const int q = __builtin_amdgcn_cvt_pk_fp8_f32(acc[g][0][r] * inv,
-                                                              acc[g][1][r] * inv, 0, false);
-                // the two lanes of a gate/up pair hold the same codes and
-                // the 32 lanes of a half the same scale: duplicate writes of
-                // equal values instead of branches
+                const int q = __builtin_amdgcn_cvt_pk_fp8_f32(h[g][0][k] * inv,
+                                                              h[g][1][k] * inv, 0, false);
+                // each (row, output) has one writer; the row scale is written
+                // by every lane holding the row (equal values, no branch)
                 otile[row * 128 + 32 * w + (rl >> 1)] = (uint8_t)q;
                 otile[row * 128 + 32 * w + 16 + (rl >> 1)] = (uint8_t)(q >> 8);
                 osc[row] = s;
