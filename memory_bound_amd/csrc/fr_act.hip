@@ -14,13 +14,18 @@
 // instruction of a wave reads one contiguous 1 KB span.  A wave walks STEPS
 // consecutive block pairs of one row with every load issued before any
 // arithmetic; the input is read once, so its loads are non-temporal in the
-// bandwidth regime.  The block maximum is a DPP row
-// reduction plus one permlane16 swap.  The scale is the correctly rounded
-// amax / 448 (fma-corrected quotient); |h / scale| <= 448 (1 + 3 ulp) < 464,
-// so the e4m3 conversion never sees a value that would overflow and needs no
+// bandwidth regime.  The block maximum is a DPP row reduction plus one
+// permlane16 swap, taken as an integer maximum (the operands are magnitudes,
+// never NaN, so their bit patterns order like the values and the DPP move
+// folds into v_max_u32; 1% faster than the float maximum, whose operands
+// need NaN canonicalisation).  The scale is the correctly rounded amax / 448
+// (fma-corrected quotient); |h / scale| <= 448 (1 + 3 ulp) < 464, so the
+// e4m3 conversion never sees a value that would overflow and needs no
 // clamp.  The wave's codes form one contiguous span (STEPS * 256 bytes);
 // they are gathered in LDS and leave as 16-byte stores (4-byte stores straight
-// from each step: 3% slower).  (Measured on MI355X at 8192 x 12288: this
+// from each step: 3% slower); its block scales are gathered in LDS too (one
+// write per block, 0.4% faster than collecting them in lanes with readlane
+// and selects).  (Measured on MI355X at 8192 x 12288: this
 // layout with 4 waves per workgroup is 5-15% faster than 2 or 8 waves per
 // workgroup or 32-byte lane-contiguous chunks.)
 //
@@ -47,9 +52,15 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
     // gathered so they leave as 16-byte stores
     constexpr int SPAN = MX ? STEPS * 136 : STEPS * 256;
     __shared__ __attribute__((aligned(16))) uint8_t obuf[4][SPAN];
-    uint8_t* ob = obuf[threadIdx.x >> 6];
+    __shared__ float sbuf[4][2 * STEPS];                 // the wave's block scales
+    // (the wave index is left in vector form: made uniform, its 64-bit
+    // division by the waves per row moves to the scalar unit and delays the
+    // first loads; measured 1% slower)
+    const int wv = (int)(threadIdx.x >> 6);
+    uint8_t* ob = obuf[wv];
+    float* sb = sbuf[wv];
     const int lane = threadIdx.x & 63;
-    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t wid = (int64_t)blockIdx.x * 4 + wv;
     if (wid >= a.waves) return;                          // whole wave exits
     const int64_t t = wid / a.wpr;
     const int wc = (int)(wid - t * a.wpr);
@@ -68,7 +79,6 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
         in[k] = NTL ? ld128_stream(row + off) : ld128(row + off);
     }
 
-    float sc = 0.0f;                                     // lane i: scale of block i
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
         float h[4];
@@ -79,16 +89,17 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
             m = fmaxf(m, fabsf(h[e]));
         }
         if constexpr (MX) {
-            m = group_reduce<8>(m, OpMax());             // block of 32 outputs
+            m = group_reduce<8>(m, OpMaxMag());          // block of 32 outputs
             const int code = mx_code(m);
             const u32 p = pack_e2m1x4(h[0], h[1], h[2], h[3], mx_mult(code));
             *reinterpret_cast<uint16_t*>(ob + (2 * k + half) * 64 + cb * 2) = (uint16_t)p;
             if ((cb & 7) == 0) ob[STEPS * 128 + (2 * k + half) * 4 + (cb >> 3)] = (uint8_t)code;
             continue;
         }
-        // Block maximum over 32 lanes (all 64 lanes take part).
-        m = group_reduce<16>(m, OpMax());
-        m = rows_pair(m, OpMax());
+        // Block maximum over 32 lanes (all 64 lanes take part); m is a
+        // maximum of magnitudes (never NaN), so the integer maximum applies.
+        m = group_reduce<16>(m, OpMaxMag());
+        m = rows_pair(m, OpMaxMag());
         const float s = div448(fmaxf(m, 1e-10f));        // correctly rounded
         const float inv = __builtin_amdgcn_rcpf(s);
         {
@@ -96,11 +107,7 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
             q = __builtin_amdgcn_cvt_pk_fp8_f32(h[2] * inv, h[3] * inv, q, true);
             *reinterpret_cast<u32*>(ob + (2 * k + half) * 128 + cb * 4) = (u32)q;
         }
-        // gather the two block scales of this step into lanes 2k and 2k+1
-        const int si = __builtin_bit_cast(int, s);
-        const float s_lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(si, 0));
-        const float s_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(si, 32));
-        sc = lane == 2 * k ? s_lo : (lane == 2 * k + 1 ? s_hi : sc);
+        if (cb == 0) sb[2 * k + half] = s;               // block 2k + half
     }
     const int b0 = wc * STEPS * 2;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -134,6 +141,7 @@ __global__ __launch_bounds__(256) void k_act(ActArgs a) {
     }
     // one contiguous store of the wave's 2 * STEPS block scales
     if (lane < 2 * STEPS && b0 + lane < a.nb) {
+        const float sc = sb[lane];
         if constexpr (NTS) __builtin_nontemporal_store(sc, srow + b0 + lane); else srow[b0 + lane] = sc;
     }
 }

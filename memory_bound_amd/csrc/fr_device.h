@@ -71,10 +71,12 @@ __device__ __forceinline__ float add_round_odd(float r, float p) {
 // with at least two fewer significand bits (e4m3 has 4) is then the correct
 // rounding of p + e.
 __device__ __forceinline__ float round_odd(float p, float e) {
-    u32 b = __float_as_uint(p);
-    if (e != 0.0f && (b & 1u) == 0u)
-        b = ((__float_as_uint(e) ^ b) >> 31) ? b - 1u : b + 1u;
-    return __uint_as_float(b);
+    const u32 b = __float_as_uint(p);
+    // +1 (away from zero) when e has the sign of p, else -1; only an even
+    // significand moves
+    const u32 dir = (u32)((int)(__float_as_uint(e) ^ b) >> 31) | 1u;
+    const u32 even = (b & 1u) - 1u;                      // all ones if b is even
+    return __uint_as_float(b + (e != 0.0f ? (dir & even) : 0u));
 }
 
 // ---------------------------------------------------------------------------
@@ -89,6 +91,13 @@ __device__ __forceinline__ float sat448(float v) {
 __device__ __forceinline__ u32 pack_e4m3x4(float a, float b, float c, float d) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+    return (u32)w;
+}
+// The same for values already known to lie within +-464 (the conversion is
+// then exact RNE and saturates at 448 by itself): no clamp.
+__device__ __forceinline__ u32 pack_e4m3x4_in_range(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (u32)w;
 }
 
@@ -123,6 +132,14 @@ struct OpSum {
 };
 struct OpMax {
     __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+// Maximum of non-negative floats (magnitudes) as unsigned integers: the bit
+// patterns of non-negative floats are ordered like the values, and the
+// integer maximum needs no NaN canonicalisation of the operands.
+struct OpMaxMag {
+    __device__ __forceinline__ float operator()(float a, float b) const {
+        return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
+    }
 };
 
 // Reduce over aligned groups of G lanes (G = 1, 2, 4, 8 or 16).

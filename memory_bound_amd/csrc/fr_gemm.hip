@@ -231,11 +231,12 @@ __global__ __launch_bounds__(256) void k_gemm_act(GemmActArgs a) {
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
+                // magnitudes, never NaN: integer maximum (no canonicalisation)
                 float m = fmaxf(fabsf(h[g][0][k]), fabsf(h[g][1][k]));
-                m = fmaxf(m, dpp_f<DPP_ROR2>(m));
-                m = fmaxf(m, dpp_f<DPP_ROR4>(m));
-                m = fmaxf(m, dpp_f<DPP_ROR8>(m));
-                m = rows_pair(m, OpMax());               // 16 lanes of parity p
+                m = OpMaxMag()(m, dpp_f<DPP_ROR2>(m));
+                m = OpMaxMag()(m, dpp_f<DPP_ROR4>(m));
+                m = OpMaxMag()(m, dpp_f<DPP_ROR8>(m));
+                m = rows_pair(m, OpMaxMag());            // 16 lanes of parity p
                 const int r = 2 * k + p;
                 // the 16 lanes of the class hold m: all write it (no branch)
                 red[(32 * g + 8 * (r >> 2) + 4 * kh + (r & 3)) * 4 + w] = m;
