@@ -40,7 +40,7 @@
 
 namespace fr {
 
-constexpr int kActSteps = 8;   // block pairs per wave (bandwidth regime)
+constexpr int kActSteps = 4;   // block pairs per wave (bandwidth regime)
 
 // STEPS: block pairs per wave; NTL / NTS: non-temporal loads / stores;
 // MX: MX FP4 output instead of block-128 FP8.
@@ -163,11 +163,13 @@ static hipError_t launch_act_cfg(const ActArgs& in, int act, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, s);
 }
 
-// Bandwidth regime (T >= 2048): 8 block pairs per wave, non-temporal loads,
+// Bandwidth regime (T >= 2048): 4 block pairs per wave, non-temporal loads,
 // cacheable stores.  Measured back to back on MI355X at 8192 x 12288 bf16
-// (~6.3 TB/s): 4, 6 or 12 pairs 1-5% slower, non-temporal stores ~5% slower,
-// cacheable loads ~15% slower.  Small batches: 2 block pairs per wave for more parallel waves,
-// everything cacheable for the next op.
+// (~6.4 TB/s): 8 pairs 1.5% slower (MX FP4 output: 2.8%), 16 pairs 5%, 2
+// pairs 11%, 1 pair 36% slower; non-temporal stores ~5% slower, cacheable
+// loads ~15% slower.  (Before the block maximum and the scale gather were
+// trimmed, 8 pairs were the fastest.)  Small batches: 2 block pairs per wave
+// for more parallel waves, everything cacheable for the next op.
 template <bool MX>
 static hipError_t launch_act_fmt(const ActArgs& a, int dtype, int act, hipStream_t s) {
     const bool big = a.T >= 2048;

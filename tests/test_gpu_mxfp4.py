@@ -62,6 +62,7 @@ ACT_CASES = [
     ("ragged_384", 7, 384, F16, oracle.ACT_SWIGLU, False, 514),
     ("smallest_128", 3, 128, BF16, oracle.ACT_GEGLU_TANH, False, 515),
     ("bench_8192", 8192, 12288, BF16, oracle.ACT_SWIGLU, True, 105),
+    ("bandwidth_ragged_1152", 2048, 1152, BF16, oracle.ACT_GEGLU_TANH, False, 517),
 ]
 
 

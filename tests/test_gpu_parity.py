@@ -249,6 +249,9 @@ ACT_CASES = [
     (5, 1152, BF16, oracle.ACT_GEGLU_TANH, True, 503),   # 9 blocks: crosses waves
     (8192, 12288, BF16, oracle.ACT_SWIGLU, True, 105),   # full bandwidth config
     (8192, 12288, BF16, oracle.ACT_GEGLU_TANH, True, 105),
+    # bandwidth launch shape (T >= 2048) with a ragged last wave per row
+    (2048, 1152, BF16, oracle.ACT_SWIGLU, True, 506),    # 9 blocks: 8 + 1
+    (2048, 640, F16, oracle.ACT_SQRELU, False, 507),     # 5 blocks: one partial wave
 ]
 
 
