@@ -28,7 +28,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 GIB = 1 << 30
 
-ACT_FP8 = "void fr::k_act<1, 0, 8, true, false, false>"
+ACT_FP8 = "void fr::k_act<1, 0, 4, true, false, false>"
 KERNELS = {  # kernel name prefix -> (op, algorithmic read bytes, write bytes)
     "void fr::k_norm<1, 2, 1, true, true, false>": (
         "resid_rmsnorm_fp8 T=8192 H=4096 bf16 MUL TOKEN",
@@ -45,7 +45,7 @@ KERNELS = {  # kernel name prefix -> (op, algorithmic read bytes, write bytes)
     "void fr::k_norm<1, 2, 1, true, true, true>": (
         "resid_rmsnorm_mxfp4 T=8192 H=4096 bf16 MUL",
         8192 * 4096 * 4 + 4096 * 2, 8192 * 4096 * 2 + 8192 * 2048 + 8192 * 128),
-    "void fr::k_act<1, 0, 8, true, false, true>": (
+    "void fr::k_act<1, 0, 4, true, false, true>": (
         "gated_act_mxfp4 T=8192 I=12288 bf16 SwiGLU",
         8192 * 24576 * 2, 8192 * 6144 + 8192 * 384),
     "void fr::k_norm<1, 2, 4, true, true, true>": (
