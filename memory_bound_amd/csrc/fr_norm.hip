@@ -439,11 +439,12 @@ struct NormShape {
 // up to 8 wavefronts (more chunks per lane only for rows wider than 8192
 // values), and in the bandwidth regime (T >= 2048) two single-wave rows per
 // workgroup and non-temporal streaming.  Measured on MI355X at T = 8192 in
-// steady state: H = 4096 bf16 at ~70% of 8 TB/s with 4 waves x 2 chunks per
-// row (2 waves x 4 chunks: 69%; 1 wave x 8 chunks: 65%; 8 waves x 1 chunk:
-// 54%; cacheable stores: 64%); H = 1024 fp16 adaptive at ~69% with 2 rows
-// per workgroup (1 or 4 rows: 65-67%).  Small batches keep the outputs
-// cacheable for the next op.
+// steady state: H = 4096 bf16 at ~73% of 8 TB/s with 4 waves x 2 chunks per
+// row (re-measured after the instruction trimming: 2 rows of 4 waves per
+// workgroup 72%, 2 waves x 4 chunks 69-70%, 1 wave x 8 chunks 66%, 8 waves x
+// 1 chunk 65%; before it, cacheable stores: 64%); H = 1024 fp16 adaptive at
+// ~69% with 2 rows per workgroup (1 or 4 rows: 65-67%).  Small batches keep
+// the outputs cacheable for the next op.
 static NormShape pick_norm_shape(int64_t T, int H, bool adaptive) {
     (void)adaptive;
     const int C = H / 8;
