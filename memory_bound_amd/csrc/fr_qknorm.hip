@@ -194,22 +194,22 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
             // weights [D] shared by the heads, or this head's slice of the
             // full-width weights (cache-resident either way)
             const void* w = p == 0 ? a.qw : a.kw;
-            const void* b = p == 0 ? a.qb : a.kb;
+            const void* b = a.norm_kind == 2 ? (p == 0 ? a.qb : a.kb) : nullptr;
             const int64_t o = a.full ? (int64_t)hl * D * 2 : 0;
-            u32x4 w0 = {0, 0, 0, 0}, w1 = w0, b0 = w0, b1 = w0;
+            // absent weights read as a pair of 16-bit ones, absent biases as
+            // zeros, so the element loop has no selects
+            const u32 one2 = DT == DT_BF16 ? 0x3F803F80u : 0x3C003C00u;
+            u32x4 w0 = {one2, one2, one2, one2}, w1 = w0;
+            u32x4 b0 = {0, 0, 0, 0}, b1 = b0;
             if (w) { w0 = ld128((const char*)w + o + off0); w1 = ld128((const char*)w + o + off1); }
             if (b) { b0 = ld128((const char*)b + o + off0); b1 = ld128((const char*)b + o + off1); }
-            const bool layer = a.norm_kind == 2;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const u32 ww = e < 4 ? w0[e] : w1[e - 4];
                 const u32 bb = e < 4 ? b0[e] : b1[e - 4];
                 const int ia = e < 4 ? 2 * e : 8 + 2 * (e - 4);
-                const float wa = w ? lo16<DT>(ww) : 1.0f, wb = w ? hi16<DT>(ww) : 1.0f;
-                const float ba = (layer && b) ? lo16<DT>(bb) : 0.0f;
-                const float bbv = (layer && b) ? hi16<DT>(bb) : 0.0f;
-                v[ia] = fmaf((v[ia] - mean[u]) * rstd[u], wa, ba);
-                v[ia + 1] = fmaf((v[ia + 1] - mean[u]) * rstd[u], wb, bbv);
+                v[ia] = fmaf((v[ia] - mean[u]) * rstd[u], lo16<DT>(ww), lo16<DT>(bb));
+                v[ia + 1] = fmaf((v[ia + 1] - mean[u]) * rstd[u], hi16<DT>(ww), hi16<DT>(bb));
             }
         }
         // rotate-half: pair e = (8j+e, D/2+8j+e); interleaved: pair m of
@@ -233,12 +233,16 @@ __global__ __launch_bounds__(256) void k_qknr(QkNormArgs a) {
                 v[b + 1] = fmaf(x1, cs, x0 * sn);
             }
         }
-        const float qs = p == 0 ? a.q_scale : 1.0f;
+        if (a.q_scale != 1.0f) {                         // uniform; 1 is the common case
+            const float qs = p == 0 ? a.q_scale : 1.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] *= qs;
+        }
         u32x4 o0, o1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            o0[e] = pack16<DT>(v[2 * e] * qs, v[2 * e + 1] * qs);
-            o1[e] = pack16<DT>(v[8 + 2 * e] * qs, v[8 + 2 * e + 1] * qs);
+            o0[e] = pack16<DT>(v[2 * e], v[2 * e + 1]);
+            o1[e] = pack16<DT>(v[8 + 2 * e], v[8 + 2 * e + 1]);
         }
         dst = p == 0 ? (char*)a.q_out + (t * a.Hq + hl) * (int64_t)D * 2
                      : (char*)a.k_out + (t * a.Hkv + hl) * (int64_t)D * 2;

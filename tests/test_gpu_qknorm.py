@@ -39,7 +39,8 @@ def run(fr, inp, case):
     q = torch.full((T, Hq, D), POISON16, dtype=torch.int16, device="cuda")
     k = torch.full((T, Hkv, D), POISON16, dtype=torch.int16, device="cuda")
     v = torch.full((T, Hkv, D), POISON16, dtype=torch.int16, device="cuda")
-    ws = [to_dev(inp[n]) for n in ("q_norm_w", "q_norm_b", "k_norm_w", "k_norm_b")]
+    ws = [None if inp[n] is None else to_dev(inp[n])
+          for n in ("q_norm_w", "q_norm_b", "k_norm_w", "k_norm_b")]
     fr.fr_qk_norm_rope(to_dev(inp["qkv"]), kind, int(full), *ws, EPS,
                        to_dev(inp["positions"]), 3 if r3 else 1, sec, theta, style,
                        qs, q, k, v, T, Hq, Hkv, D, dt)
@@ -61,3 +62,30 @@ def test_qk_norm_rope(fr, case):
     sk = check16(kg, ko, dt, "k_out")
     check_exact(vg, vo, "v_out")
     announce(f"  bit-identical q {sq:.6f} k {sk:.6f}")
+
+
+ABSENT_CASES = [
+    # (case, which optional inputs are absent): weights read as 1, biases as 0
+    (("rms_head_noweight", 20, 8, 2, 128, BF16, 1, False, False, None, 0, 1e4, 1.0, 611), "wb"),
+    (("layer_full_nobias", 12, 4, 4, 64, F16, 2, True, False, None, 1, 1e4, 0.5, 612), "b"),
+    (("layer_head_noweight", 9, 6, 3, 128, BF16, 2, False, True, (22, 21, 21), 0, 1e4, 1.0, 613), "w"),
+]
+
+
+@pytest.mark.parametrize("case,absent", ABSENT_CASES, ids=lambda c: c[0] if isinstance(c, tuple) else c)
+def test_qk_norm_rope_absent_weights(fr, case, absent):
+    name, T, Hq, Hkv, D, dt, kind, full, r3, sec, style, theta, qs, seed = case
+    announce(f"qk_norm_rope {name}: absent {absent}")
+    inp = workloads.qk_norm_rope_inputs(T, Hq, Hkv, D, dt, seed, scope_full=full, rope3=r3)
+    for n in ("q_norm_w", "k_norm_w") if "w" in absent else ():
+        inp[n] = None
+    for n in ("q_norm_b", "k_norm_b") if "b" in absent else ():
+        inp[n] = None
+    qg, kg, vg = run(fr, inp, case)
+    qo, ko, vo = oracle.qk_norm_rope(
+        inp["qkv"], kind, int(full), inp["q_norm_w"], inp["q_norm_b"], inp["k_norm_w"],
+        inp["k_norm_b"], EPS, inp["positions"], 3 if r3 else 1, sec, theta, style, qs,
+        Hq, Hkv, D, dt)
+    check16(qg, qo, dt, "q_out")
+    check16(kg, ko, dt, "k_out")
+    check_exact(vg, vo, "v_out")
