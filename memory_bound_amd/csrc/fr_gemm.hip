@@ -13,7 +13,8 @@
 // W e4m3 and fp32 dequant scales; n = 2j is gate output j, n = 2j+1 its up
 // partner.  Each workgroup (4 waves) owns a tile of 32 RG rows x 256
 // columns, i.e. exactly one 128-output block of the result per row, so the
-// block maximum never leaves the workgroup.  Wave w computes columns
+// block maximum never leaves the workgroup (large batches use a 128-row,
+// 8-wave variant, k_gemm_act_big, below).  Wave w computes columns
 // [64w, 64w+64) of all the tile's rows as 2 RG tiles of 32x32 with
 // v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, unit MX scales), in
 // transposed form (weight fragment first; see the kernel): per 128-wide K
@@ -278,6 +279,197 @@ __global__ __launch_bounds__(256) void k_gemm_act(GemmActArgs a) {
     }
 }
 
+// Large-batch tile: 128 rows x 256 columns per workgroup of 8 waves, both
+// operands staged through LDS.  Wave w computes rows [64 (w / 4), +64) x
+// columns [64 (w % 4), +64) in the transposed form above.  Per K block the
+// workgroup fetches 16 KB of activation and 32 KB of weight fragments once
+// (each wave one 4 KB packed column group and two 1 KB activation chunks,
+// DEPTH blocks ahead in registers) and every wave reads its fragments from
+// the double-buffered stage; the weight bytes per output are half those of
+// the 64-row tile, whose waves load their own weight fragments.
+constexpr int kBigPanel = 4096;     // rows x K blocks of the staged a_s panel (128 x 32)
+
+template <int ACT, int DEPTH>
+__global__ __launch_bounds__(512) void k_gemm_act_big(GemmActArgs a) {
+    constexpr int ROWS = 128;
+    static_assert(DEPTH % 2 == 0, "stage parity must be static");
+    __shared__ __attribute__((aligned(16))) uint8_t astage[2][16384];      // [rg][chunk][lane]
+    __shared__ __attribute__((aligned(16))) uint8_t wstage[2][32768];      // [cg][chunk][lane]
+    __shared__ __attribute__((aligned(16))) float asp[kBigPanel];          // [kb][row]
+    __shared__ __attribute__((aligned(16))) float bsp[2 * kGemmMaxKB];     // [block][kb]
+    __shared__ __attribute__((aligned(16))) float red[ROWS * 4];           // [row][col quarter]
+    __shared__ __attribute__((aligned(16))) float osc[ROWS];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;                      // 0..7
+    const int wr = w >> 2, wc = w & 3;                   // row half, column quarter
+    const int L = (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
+    if (L >= a.tiles) return;                            // whole workgroup exits
+    const int n_tile = L / a.mt;
+    const int m_tile = L - n_tile * a.mt;
+    const int m0 = m_tile * ROWS;
+    const int KB = a.K >> 7;
+    const int KBp = (KB + DEPTH - 1) / DEPTH * DEPTH;
+    const int rl = lane & 31;
+    const int kh = lane >> 5;
+
+    // scale panels (see k_gemm_act)
+    constexpr int PJ = kBigPanel / 512;
+    float sv[PJ];
+#pragma unroll
+    for (int j = 0; j < PJ; ++j) {
+        const int e = min((int)threadIdx.x + 512 * j, ROWS * KB - 1);
+        const int kb = e / ROWS, row = e - kb * ROWS;
+        sv[j] = a.a_scales[(int64_t)min(m0 + row, a.M - 1) * KB + kb];
+    }
+    const int tb = min((int)threadIdx.x, 2 * KB - 1);
+    const float bv = a.b_scales[(int64_t)(2 * n_tile) * KB + tb];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // This wave's global fetch per K block: activation chunks c0 = w and
+    // c1 = w + 8 of the 16 (row group c / 4, chunk c % 4), and packed weight
+    // column group w (4 chunks).
+    const uint8_t* ag0 = a.A + (int64_t)min(m0 + 32 * (w >> 2) + rl, a.M - 1) * a.K
+                         + chunk_koff(w & 3, kh);
+    const uint8_t* ag1 = a.A + (int64_t)min(m0 + 32 * (2 + (w >> 2)) + rl, a.M - 1) * a.K
+                         + chunk_koff(w & 3, kh);
+    const uint8_t* bq = a.B + (int64_t)(8 * n_tile + w) * KB * 4096 + lane * 16;
+
+    u32x4 ra0[DEPTH], ra1[DEPTH], rw[DEPTH][4];
+    auto issue = [&](int d, int kb) {
+        const int o = kb * 4096;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) rw[d][c] = ld128(bq + o + c * 1024);
+        ra0[d] = ld128(ag0 + kb * 128);
+        ra1[d] = ld128(ag1 + kb * 128);
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(d, min(d, KB - 1));
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int j = 0; j < PJ; ++j) asp[threadIdx.x + 512 * j] = sv[j];
+    if (threadIdx.x < 2 * kGemmMaxKB) bsp[threadIdx.x] = bv;
+
+    f32x16 acc[2][2];                                    // [row group][column group]
+#pragma unroll
+    for (int g = 0; g < 2; ++g) acc[g][0] = acc[g][1] = f32x16{};
+    const float* bsw = bsp + (wc >> 1) * KB;
+    for (int kb0 = 0; kb0 < KBp; kb0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int kb = kb0 + d;
+            uint8_t* as = astage[d & 1] + lane * 16;
+            uint8_t* ws = wstage[d & 1] + lane * 16;
+            *reinterpret_cast<u32x4*>(as + w * 1024) = ra0[d];
+            *reinterpret_cast<u32x4*>(as + (w + 8) * 1024) = ra1[d];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(ws + (w * 4 + c) * 1024) = rw[d][c];
+            __syncthreads();                             // stage (and panels) complete
+            i32x8 fa[2][2], fb[2][2];                    // [group][K step]
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const int rg = 2 * wr + g, cg = 2 * wc + g;
+                fa[g][0] = join(lds128(as + (rg * 4 + 0) * 1024), lds128(as + (rg * 4 + 1) * 1024));
+                fa[g][1] = join(lds128(as + (rg * 4 + 2) * 1024), lds128(as + (rg * 4 + 3) * 1024));
+                fb[g][0] = join(lds128(ws + (cg * 4 + 0) * 1024), lds128(ws + (cg * 4 + 1) * 1024));
+                fb[g][1] = join(lds128(ws + (cg * 4 + 2) * 1024), lds128(ws + (cg * 4 + 3) * 1024));
+            }
+            const int kbc = min(kb, KB - 1);
+            const float bk = kb < KB ? bsw[kbc] : 0.0f;
+            float f[2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) f[g] = asp[kbc * ROWS + 32 * (2 * wr + g) + rl] * bk;
+            f32x16 p[2][2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    p[g][t] = mma_e4m3(fb[t][0], fa[g][0], f32x16{});
+                    p[g][t] = mma_e4m3(fb[t][1], fa[g][1], p[g][t]);
+                }
+            }
+            issue(d, min(kb + DEPTH, KB - 1));
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    acc[g][0][r] = fmaf(p[g][0][r], f[g], acc[g][0][r]);
+                    acc[g][1][r] = fmaf(p[g][1][r], f[g], acc[g][1][r]);
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < 2; ++g) asm volatile("" : "+v"(acc[g][0]), "+v"(acc[g][1]));
+        }
+    }
+
+    // Epilogue as in k_gemm_act; this wave's outputs of the block are
+    // j = 32 wc + 16 t + 4 (i / 2) + 2 kh + i % 2 for rows 64 wr + 32 g + rl.
+    float h[2][2][8];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        float m = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                h[g][t][i] = gate_act<ACT>(acc[g][t][2 * i]) * acc[g][t][2 * i + 1];
+                m = fmaxf(m, fabsf(h[g][t][i]));
+            }
+        }
+        m = halves(m, OpMaxMag());
+        red[(64 * wr + 32 * g + rl) * 4 + wc] = m;
+    }
+    __syncthreads();                                     // stages are reused below
+    uint8_t* otile = astage[0];                          // [row][128] codes (16 KB)
+    const int nbo = a.I >> 7;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int row = 64 * wr + 32 * g + rl;
+        const float4 mm = *reinterpret_cast<const float4*>(red + row * 4);
+        const float mx = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
+        const float s = div448(fmaxf(mx, 1e-10f));
+        const float inv = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+                const int q = __builtin_amdgcn_cvt_pk_fp8_f32(h[g][t][2 * i2] * inv,
+                                                              h[g][t][2 * i2 + 1] * inv, 0, false);
+                *reinterpret_cast<uint16_t*>(otile + row * 128 + 32 * wc + 16 * t + 4 * i2 + 2 * kh) =
+                    (uint16_t)q;
+            }
+        }
+        osc[row] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < ROWS && m0 + (int)threadIdx.x < a.M)
+        a.out_scales[(int64_t)(m0 + threadIdx.x) * nbo + n_tile] = osc[threadIdx.x];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = (w + 8 * i) * 8 + (lane >> 3);
+        if (m0 + row < a.M)
+            st128(a.out + (int64_t)(m0 + row) * a.I + n_tile * 128 + (lane & 7) * 16,
+                  lds128(otile + row * 128 + (lane & 7) * 16));
+    }
+}
+
+template <int DEPTH>
+static hipError_t launch_gemm_big(const GemmActArgs& in, int act, hipStream_t s) {
+    GemmActArgs a = in;
+    a.mt = (a.M + 127) / 128;
+    a.tiles = a.mt * (a.I / 128);
+    a.per_xcd = (a.tiles + 7) / 8;
+    const void* fn;
+    switch (act) {
+    case ACT_SWIGLU: fn = (const void*)k_gemm_act_big<ACT_SWIGLU, DEPTH>; break;
+    case ACT_GEGLU_TANH: fn = (const void*)k_gemm_act_big<ACT_GEGLU_TANH, DEPTH>; break;
+    default: fn = (const void*)k_gemm_act_big<ACT_SQRELU, DEPTH>; break;
+    }
+    void* args[] = {&a};
+    return hipLaunchKernel(fn, dim3((unsigned)(8 * a.per_xcd)), dim3(512), args, 0, s);
+}
+
 template <int RG, int DEPTH>
 static hipError_t launch_gemm_cfg(const GemmActArgs& in, int act, hipStream_t s) {
     GemmActArgs a = in;
@@ -301,9 +493,17 @@ static hipError_t launch_gemm_cfg(const GemmActArgs& in, int act, hipStream_t s)
 // vs 192 tiles, 26.1 vs 19.1 us); 128-row tiles, 4 K blocks in flight, and
 // waves loading their own activation fragments (no LDS stage) were never
 // faster.
+//
+// Large batches take the 128-row, 8-wave tile once it gives at least three
+// workgroups per CU (measured, outputs identical: 2048 x 2048 x 6144 88.0 ->
+// 81.9 us, 2048 x 4096 x 12288 309 -> 286 us, 4096 x 4096 x 12288 596 -> 570
+// us; with 1.5 rounds of workgroups it loses: 1024 x 2048 x 6144 46.6 ->
+// 52.5 us, 512 x 4096 x 12288 82 -> 90 us).
 hipError_t launch_gemm_act(const GemmActArgs& in, int act, hipStream_t s) {
     const int64_t nt = in.I / 128;
     const int KB = in.K / 128;
+    if (128 * KB <= kBigPanel && ((int64_t)in.M + 127) / 128 * nt >= 768)
+        return launch_gemm_big<2>(in, act, s);
     if (64 * KB <= kGemmPanel && ((int64_t)in.M + 63) / 64 * nt >= 192)
         return launch_gemm_cfg<2, 2>(in, act, s);
     return launch_gemm_cfg<1, 2>(in, act, s);

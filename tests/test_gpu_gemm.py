@@ -182,6 +182,26 @@ def test_gemm_bench_shapes(fr):
     announce(f"  sampled rows {len(rows)}: fp8 identical {ident:.6f}, scale max rel err {rel:.2e}")
 
 
+def test_gemm_large_batch_tile_ragged(fr):
+    """The 128-row, 8-wave tile (taken at >= 768 tiles of 128 rows) with a
+    ragged last row tile: M = 2000 = 15 x 128 + 80, checked on sampled rows
+    (rows are independent) including both sides of every tile edge."""
+    M, K, I = 2000, 512, 6144
+    announce(f"gemm_gated_act large-batch tile M={M} K={K} I={I}, sampled rows")
+    inp = workloads.gemm_inputs(M, K, I, 2000)
+    for act in (oracle.ACT_SWIGLU, oracle.ACT_SQRELU):
+        q_g, s_g = run_gemm(fr, inp, act)
+        rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 127, 128, 1919, 1920,
+                                          1951, 1952, M - 2, M - 1],
+                                         np.random.default_rng(2000).integers(0, M, 10)]))
+        sub = {"a": inp["a"][rows], "a_scales": inp["a_scales"][rows],
+               "w": inp["w"], "w_scales": inp["w_scales"]}
+        q_o, s_o, _ = oracle.gemm_gated_act_fp8(sub["a"], sub["a_scales"], sub["w"],
+                                                sub["w_scales"], act)
+        ident, rel = check_gemm_interval(q_g[rows], s_g[rows], q_o, s_o, sub, act)
+        announce(f"  act {act}: sampled rows {len(rows)}: fp8 identical {ident:.6f}")
+
+
 def test_gemm_worked_example(fr):
     announce("gemm worked example")
     K, I = 128, 128
