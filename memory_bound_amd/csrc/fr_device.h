@@ -50,21 +50,6 @@ __device__ __forceinline__ u32 pack16(float a, float b) {
     }
 }
 
-// r + p rounded to fp32 with round-to-odd: the exact error of the fp32 sum
-// (TwoSum) decides whether an even result is moved one ulp towards the exact
-// value.  Rounding this value once more to a format with at most 22 bits of
-// precision (fp16, bf16) gives the correctly rounded exact sum, because fp32
-// keeps at least two extra bits.
-__device__ __forceinline__ float add_round_odd(float r, float p) {
-    const float s = r + p;
-    const float bb = s - r;
-    const float e = (r - (s - bb)) + (p - bb);
-    u32 sb = __float_as_uint(s);
-    if (e != 0.0f && (sb & 1u) == 0u)
-        sb = ((e > 0.0f) == (s > 0.0f)) ? sb + 1u : sb - 1u;
-    return __uint_as_float(sb);
-}
-
 // Round-to-odd of the exact value p + e, where p = fp32(p + e) and e is the
 // (small) remainder: if e != 0 and p's last significand bit is even, step one
 // ulp towards the exact value.  A later rounding of the result to a format
@@ -77,6 +62,20 @@ __device__ __forceinline__ float round_odd(float p, float e) {
     const u32 dir = (u32)((int)(__float_as_uint(e) ^ b) >> 31) | 1u;
     const u32 even = (b & 1u) - 1u;                      // all ones if b is even
     return __uint_as_float(b + (e != 0.0f ? (dir & even) : 0u));
+}
+
+// r + p rounded to fp32 with round-to-odd: TwoSum gives s = fp32(r + p) and
+// the exact error e of that sum, and round_odd moves an even s one ulp
+// towards the exact value.  Rounding the result once more to a format with
+// at most 22 bits of precision (fp16, bf16) gives the correctly rounded exact
+// sum, because fp32 keeps at least two extra bits.  (s is 0 only when r + p
+// is exactly 0: a sum of two fp32 values that rounds to 0 is representable,
+// so e is 0 there and no step is taken.)
+__device__ __forceinline__ float add_round_odd(float r, float p) {
+    const float s = r + p;
+    const float bb = s - r;
+    const float e = (r - (s - bb)) + (p - bb);
+    return round_odd(s, e);
 }
 
 // ---------------------------------------------------------------------------
