@@ -189,7 +189,7 @@ def test_gemm_large_batch_tile_ragged(fr):
     M, K, I = 2000, 512, 6144
     announce(f"gemm_gated_act large-batch tile M={M} K={K} I={I}, sampled rows")
     inp = workloads.gemm_inputs(M, K, I, 2000)
-    for act in (oracle.ACT_SWIGLU, oracle.ACT_SQRELU):
+    for act in (oracle.ACT_SWIGLU, oracle.ACT_GEGLU_TANH, oracle.ACT_SQRELU):
         q_g, s_g = run_gemm(fr, inp, act)
         rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 127, 128, 1919, 1920,
                                           1951, 1952, M - 2, M - 1],
