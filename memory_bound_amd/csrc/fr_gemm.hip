@@ -84,6 +84,36 @@ __device__ __forceinline__ int chunk_koff(int c, int kh) {
     return 64 * (c >> 1) + 32 * kh + 16 * (c & 1);
 }
 
+// Output tile in LDS: [row][128] codes, the 16-byte chunk c of a row kept at
+// chunk c ^ (row % 8), so that the 32 rows of one store (rows 128 bytes
+// apart) spread over the banks.
+__device__ __forceinline__ int otile_off(int row, int chunk) {
+    return row * 128 + ((chunk ^ (row & 7)) << 4);
+}
+
+// Store one row's codes of a 32-output quarter q (two 16-output tiles t).
+// c[t][i] holds the codes of outputs 16 t + 4 i + 2 kh + {0, 1}, so each
+// lane half has two of every four bytes; one permlane32 swap per tile hands
+// each lane the partner's half of the dwords it writes (lane half 0 the
+// first 8 bytes of the tile, half 1 the last 8), one 8-byte store each.
+__device__ __forceinline__ void store_codes(uint8_t* otile, int row, int q, int kh,
+                                            const u32 (&c)[2][4]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const u32 send = kh ? (c[t][0] | c[t][1] << 16) : (c[t][2] | c[t][3] << 16);
+        const auto pr = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+        const u32 recv = kh ? (u32)pr[0] : (u32)pr[1];
+        const u32 lo0 = kh ? (recv & 0xFFFFu) : c[t][0];
+        const u32 hi0 = kh ? c[t][2] : (recv & 0xFFFFu);
+        const u32 lo1 = kh ? (recv >> 16) : c[t][1];
+        const u32 hi1 = kh ? c[t][3] : (recv >> 16);
+        u32x2 v;
+        v.x = lo0 | hi0 << 16;
+        v.y = lo1 | hi1 << 16;
+        *reinterpret_cast<u32x2*>(otile + otile_off(row, 2 * q + t) + 8 * kh) = v;
+    }
+}
+
 // RG: 32-row groups per tile (32 RG x K/128 <= kGemmPanel); DEPTH: K blocks
 // in flight per wave (even, so the LDS stage of a block is static).
 //
@@ -252,17 +282,16 @@ __global__ __launch_bounds__(256) void k_gemm_act(GemmActArgs a) {
         const float mx = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
         const float s = div448(fmaxf(mx, 1e-10f));       // correctly rounded
         const float inv = __builtin_amdgcn_rcpf(s);
+        // |h * inv| <= 448 (1 + 3 ulp) < 464: no clamp needed
+        u32 c[2][4];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-                // |h * inv| <= 448 (1 + 3 ulp) < 464: no clamp needed
-                const int q = __builtin_amdgcn_cvt_pk_fp8_f32(h[g][t][2 * i2] * inv,
-                                                              h[g][t][2 * i2 + 1] * inv, 0, false);
-                *reinterpret_cast<uint16_t*>(otile + row * 128 + 32 * w + 16 * t + 4 * i2 + 2 * kh) =
-                    (uint16_t)q;
-            }
+            for (int i2 = 0; i2 < 4; ++i2)
+                c[t][i2] = (u32)__builtin_amdgcn_cvt_pk_fp8_f32(h[g][t][2 * i2] * inv,
+                                                               h[g][t][2 * i2 + 1] * inv, 0, false);
         }
+        store_codes(otile, row, w, kh, c);
         osc[row] = s;                                    // equal values from every writer
     }
     __syncthreads();
@@ -274,7 +303,7 @@ __global__ __launch_bounds__(256) void k_gemm_act(GemmActArgs a) {
             const int row = (w + 4 * i) * 8 + (lane >> 3);
             if (m0 + row < a.M)
                 st128(a.out + (int64_t)(m0 + row) * a.I + n_tile * 128 + (lane & 7) * 16,
-                      lds128(otile + row * 128 + (lane & 7) * 16));
+                      lds128(otile + otile_off(row, lane & 7)));
         }
     }
 }
@@ -430,16 +459,15 @@ __global__ __launch_bounds__(512) void k_gemm_act_big(GemmActArgs a) {
         const float mx = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
         const float s = div448(fmaxf(mx, 1e-10f));
         const float inv = __builtin_amdgcn_rcpf(s);
+        u32 c[2][4];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-                const int q = __builtin_amdgcn_cvt_pk_fp8_f32(h[g][t][2 * i2] * inv,
-                                                              h[g][t][2 * i2 + 1] * inv, 0, false);
-                *reinterpret_cast<uint16_t*>(otile + row * 128 + 32 * wc + 16 * t + 4 * i2 + 2 * kh) =
-                    (uint16_t)q;
-            }
+            for (int i2 = 0; i2 < 4; ++i2)
+                c[t][i2] = (u32)__builtin_amdgcn_cvt_pk_fp8_f32(h[g][t][2 * i2] * inv,
+                                                               h[g][t][2 * i2 + 1] * inv, 0, false);
         }
+        store_codes(otile, row, wc, kh, c);
         osc[row] = s;
     }
     __syncthreads();
@@ -450,7 +478,7 @@ __global__ __launch_bounds__(512) void k_gemm_act_big(GemmActArgs a) {
         const int row = (w + 8 * i) * 8 + (lane >> 3);
         if (m0 + row < a.M)
             st128(a.out + (int64_t)(m0 + row) * a.I + n_tile * 128 + (lane & 7) * 16,
-                  lds128(otile + row * 128 + (lane & 7) * 16));
+                  lds128(otile + otile_off(row, lane & 7)));
     }
 }
 
