@@ -43,8 +43,10 @@
 // columns per 32-column group, gate and up partner in adjacent registers,
 // so act(g) * u needs no lane exchange.  Row maxima are reduced over the
 // lane's values, the other lane half and the 4 waves (LDS); the codes go
-// through LDS so each output row leaves as 128 contiguous bytes, and the
-// row scales are gathered in LDS and leave as one store.  Lanes that hold
+// through LDS so each output row leaves as 128 contiguous bytes (8-byte
+// stores into a row-swizzled tile, free of bank conflicts: 4-9% faster
+// than one 2-byte store per output pair, whose 32 rows shared one bank),
+// and the row scales are gathered in LDS and leave as one store.  Lanes that hold
 // the same value all write it, so the epilogue has no per-row branches (it
 // was ~20% of the kernel at 128 tokens with them).  Tiles are ordered so
 // that each XCD (which serves blocks b with b % 8 fixed) walks a contiguous
