@@ -62,6 +62,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGemmMaxKB = 128;     // K <= 16384
 constexpr int kGemmPanel = 4096;    // rows x K blocks of the staged a_s panel
+constexpr int kCUs = 256;           // compute units of an MI355X
 
 __device__ __forceinline__ i32x8 join(u32x4 lo, u32x4 hi) {
     i32x8 r;
@@ -519,10 +520,12 @@ static hipError_t launch_gemm_cfg(const GemmActArgs& in, int act, hipStream_t s)
 // Row groups per tile.  Measured on MI355X (hidden 2048 / 4096, inter 6144 /
 // 12288, 128 to 4096 tokens): 64-row tiles win once they still give three
 // quarters of the 256 CUs a tile (128 x 4096 x 12288: 192 tiles, 41.7 us vs
-// 47.1 us with 32-row tiles), 32-row tiles otherwise (128 x 2048 x 6144: 96
-// vs 192 tiles, 26.1 vs 19.1 us); 128-row tiles, 4 K blocks in flight, and
-// waves loading their own activation fragments (no LDS stage) were never
-// faster.
+// 47.1 us with 32-row tiles), and also once 32-row tiles would need more
+// than one workgroup on some CUs (192 x 2048 x 6144: 144 tiles of 64 rows
+// 18.4 us vs 288 of 32 rows 19.9 us); 32-row tiles otherwise (128 x 2048 x
+// 6144: 96 vs 192 tiles, 26.1 vs 19.1 us; 160 x 2048 x 6144: 144 vs 240
+// tiles, 17.9 vs 15.5 us); 128-row tiles, 4 K blocks in flight, and waves
+// loading their own activation fragments (no LDS stage) were never faster.
 //
 // Large batches take the 128-row, 8-wave tile once it gives at least three
 // workgroups per CU (measured, outputs identical: 2048 x 2048 x 6144 88.0 ->
@@ -534,7 +537,8 @@ hipError_t launch_gemm_act(const GemmActArgs& in, int act, hipStream_t s) {
     const int KB = in.K / 128;
     if (128 * KB <= kBigPanel && ((int64_t)in.M + 127) / 128 * nt >= 768)
         return launch_gemm_big<2>(in, act, s);
-    if (64 * KB <= kGemmPanel && ((int64_t)in.M + 63) / 64 * nt >= 192)
+    if (64 * KB <= kGemmPanel && (((int64_t)in.M + 63) / 64 * nt >= 192 ||
+                                  ((int64_t)in.M + 31) / 32 * nt > kCUs))
         return launch_gemm_cfg<2, 2>(in, act, s);
     return launch_gemm_cfg<1, 2>(in, act, s);
 }
