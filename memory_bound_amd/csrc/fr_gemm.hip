@@ -531,14 +531,19 @@ static hipError_t launch_gemm_cfg(const GemmActArgs& in, int act, hipStream_t s)
 // workgroups per CU (measured, outputs identical: 2048 x 2048 x 6144 88.0 ->
 // 81.9 us, 2048 x 4096 x 12288 309 -> 286 us, 4096 x 4096 x 12288 596 -> 570
 // us; with 1.5 rounds of workgroups it loses: 1024 x 2048 x 6144 46.6 ->
-// 52.5 us, 512 x 4096 x 12288 82 -> 90 us).
+// 52.5 us, 512 x 4096 x 12288 82 -> 90 us), and also when its tiles fit in
+// one round while 64-row tiles would not (512 x 2048 x 6144: 192 tiles
+// 25.1 us vs 384 tiles of 64 rows 28.7 us; 384 x 2048 x 6144: 24.7 vs
+// 25.2 us; with more than one round of its own it loses: 768 x 2048 x 6144
+// 44.2 vs 39.8 us, 384 x 4096 x 12288 82.7 vs 73.8 us).
 hipError_t launch_gemm_act(const GemmActArgs& in, int act, hipStream_t s) {
     const int64_t nt = in.I / 128;
     const int KB = in.K / 128;
-    if (128 * KB <= kBigPanel && ((int64_t)in.M + 127) / 128 * nt >= 768)
+    const int64_t t128 = ((int64_t)in.M + 127) / 128 * nt;
+    const int64_t t64 = ((int64_t)in.M + 63) / 64 * nt;
+    if (128 * KB <= kBigPanel && (t128 >= 768 || (t128 <= kCUs && t64 > kCUs)))
         return launch_gemm_big<2>(in, act, s);
-    if (64 * KB <= kGemmPanel && (((int64_t)in.M + 63) / 64 * nt >= 192 ||
-                                  ((int64_t)in.M + 31) / 32 * nt > kCUs))
+    if (64 * KB <= kGemmPanel && (t64 >= 192 || ((int64_t)in.M + 31) / 32 * nt > kCUs))
         return launch_gemm_cfg<2, 2>(in, act, s);
     return launch_gemm_cfg<1, 2>(in, act, s);
 }

@@ -138,7 +138,7 @@ GEMM_CASES = [
     (192, 2048, 6144, oracle.ACT_SWIGLU, 705),           # 2B gate_up, S=192
     (192, 2048, 6144, oracle.ACT_GEGLU_TANH, 705),
     (128, 4096, 12288, oracle.ACT_SWIGLU, 706),          # 8B gate_up, S=128
-    (390, 2048, 6144, oracle.ACT_SWIGLU, 708),           # 64-row tiles, ragged
+    (390, 2048, 6144, oracle.ACT_SWIGLU, 708),           # 128-row tiles (one round), ragged
     (1000, 2048, 6144, oracle.ACT_SQRELU, 709),          # 64-row tiles (768), ragged
     (1024, 4096, 6144, oracle.ACT_SWIGLU, 710),          # 64-row tiles, K = 4096
     (96, 16384, 256, oracle.ACT_SWIGLU, 711),            # largest K
