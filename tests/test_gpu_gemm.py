@@ -2,20 +2,33 @@
 block-128 FP8 output, against the oracle (dequantise, float64 matmul,
 activation, block quantisation) on the same seeded codes and scales.
 
-Acceptance (derived from the arithmetic).  The gfx950 e4m3 matrix
-instruction sums its 64 exact products with a bounded error: measured on
-N(0,1)-scaled codes, |err| <= 2^-14.9 * sum|a b| for one instruction.  The
-kernel adds the two instructions of a 128-wide K block, scales the block
-sum and accumulates in fp32, so each accumulator carries
-|d acc| <= U * sum_k |a_k w_k| with U = 2^-13 (the measured bound with a
-margin of ~3.7x; fp32 terms are negligible beside it).  With S = sum|a w|
-(from the oracle's operands) and g, u the oracle's exact gate/up values:
+Acceptance (derived from the arithmetic; the matrix instruction's own error
+is measured by test_mfma_block_error_bound below).  The kernel forms each
+128-wide K block's partial sum p_b with two e4m3 matrix instructions
+(v_mfma_scale_f32_32x32x64_f8f6f4) starting from zero, then folds
+acc = fma(p_b, a_s * w_s, acc) in fp32.  The products of e4m3 codes are
+exact, but the instruction does not add them exactly: its error on one
+block is bounded by C_MFMA times the block's largest product magnitude,
+|p_b - P_b| <= C_MFMA * max_k |a_k w_k|, with C_MFMA = 2^-10 (the probe
+test asserts it on six operand classes; the largest ratio seen on MI355X is
+2^-10.7).  Relative to the sum of magnitudes the same error is 2^-15 on the
+GEMM's N(0,1)-shaped codes but 2^-12 on codes of wide dynamic range, so a
+bound in the sum of magnitudes would depend on the data; the maximum-based
+one does not.  Bounding each block's largest product by the product of the
+two operands' block maxima (amax_b, wmax_b, dequantised), and adding the
+fp32 fold (the scale product and one fma per block, 2^-24 each, against the
+running sum <= S = sum_k |A_k W_k|), every accumulator lies within
+  E_acc = C_MFMA * sum_b amax_b(m) wmax_b(n) + (K/128 + 2) 2^-24 S(m, n)
+of the exact dequantised sum.  With g, u the oracle's exact gate and up
+values and dg, du their E_acc:
   E_h = |act'|max * dg * (|u| + du) + (|act(g)| + |act'|max * dg) * du,
-  dg = U * S_g, du = U * S_u, |act'| <= 1.2 for SiLU and GELU-tanh,
-  2 (|g| + dg) for ReLU^2.
+  |act'| <= 1.2 for SiLU and GELU-tanh, 2 (|g| + dg) for ReLU^2.
 Every GPU code must lie in the e4m3 code interval of (h_o -+ E_h) / s_gpu,
 and every GPU scale within max_block(E_h) / 448 (+ 4 ulp) of the oracle's.
-The identical fraction is reported."""
+So the fp8 rule of the element-wise ops (>= 99.9% identical codes, scales
+within 1e-6) is replaced here by this interval rule: where the interval
+holds one code the GPU code must be that code; the identical fraction and
+the fraction of codes whose interval holds a single code are reported."""
 import numpy as np
 import pytest
 import torch
@@ -33,7 +46,7 @@ def fr():
     return memory_bound_amd
 
 
-U_MFMA = 2.0 ** -13
+C_MFMA = 2.0 ** -10          # per 128-wide K block, times the largest |product|
 
 
 def _act(g, act):
@@ -49,15 +62,29 @@ def _ord(c):
     return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
 
 
+def accumulator_bound(inp):
+    """E_acc of every output (see the module docstring): [M, 2I] float64."""
+    tab = oracle.e4m3_table()
+    a, w = inp["a"], inp["w"]
+    M, K = a.shape
+    N = w.shape[0]
+    KB = K // 128
+    amax = np.abs(tab[a]).reshape(M, KB, 128).max(axis=2) * inp["a_scales"]
+    wmax = np.abs(tab[w]).reshape(N, KB, 128).max(axis=2) \
+        * np.repeat(inp["w_scales"].astype(np.float64), 128, axis=0)
+    A = oracle.dequant_blocks(a, inp["a_scales"], 1)
+    W = oracle.dequant_blocks(w, inp["w_scales"], 128)
+    S = np.abs(A) @ np.abs(W).T
+    return C_MFMA * (amax @ wmax.T) + (KB + 2) * 2.0 ** -24 * S, A @ W.T
+
+
 def check_gemm_interval(q_g, s_g, q_o, s_o, inp, act):
     """Interval parity (see the module docstring); returns (identical
-    fraction, max scale relative error)."""
-    A = oracle.dequant_blocks(inp["a"], inp["a_scales"], 1)
-    W = oracle.dequant_blocks(inp["w"], inp["w_scales"], 128)
-    acc = A @ W.T
-    S = np.abs(A) @ np.abs(W).T
+    fraction, fraction of single-code intervals, max scale relative
+    error)."""
+    E_acc, acc = accumulator_bound(inp)
     g, u = acc[:, 0::2], acc[:, 1::2]
-    dg, du = U_MFMA * S[:, 0::2], U_MFMA * S[:, 1::2]
+    dg, du = E_acc[:, 0::2], E_acc[:, 1::2]
     h = _act(g, act) * u
     dmax = 2.0 * (np.abs(g) + dg) if act == oracle.ACT_SQRELU else 1.2
     E = dmax * dg * (np.abs(u) + du) + (np.abs(_act(g, act)) + dmax * dg) * du
@@ -82,9 +109,83 @@ def check_gemm_interval(q_g, s_g, q_o, s_o, inp, act):
         raise AssertionError(f"{out.sum()} codes outside their interval; first {tuple(i)}: "
                              f"got {q_g[tuple(i)]:#04x} interval [{lo[tuple(i)]:#04x}, "
                              f"{hi[tuple(i)]:#04x}] oracle {q_o[tuple(i)]:#04x}")
-    ident = float(np.mean((q_g == q_o) | (((q_g | q_o) & 0x7F) == 0)))
-    assert ident >= 0.99, f"only {ident:.6f} identical"
-    return ident, float((np.abs(s_g64 - s_o) / s_o).max())
+    same = lambda x, y: (x == y) | (((x | y) & 0x7F) == 0)       # +-0 identified
+    ident = float(np.mean(same(q_g, q_o)))
+    single = float(np.mean(same(lo, hi)))
+    return ident, single, float((np.abs(s_g64 - s_o) / s_o).max())
+
+
+# ---------------------------------------------------------------------------
+# The matrix instruction's accumulation error, measured against exact sums
+# ---------------------------------------------------------------------------
+
+def _probe_tiles(kind, n, rng):
+    """n operand tile pairs [n, 32, 128] of e4m3 codes of one class."""
+    shape = (n, 32, 128)
+    if kind == "workload":            # the GEMM inputs' class: N(0,1) x 32
+        draw = lambda: workloads.e4m3_codes(workloads.normal(rng, shape) * np.float32(32.0))
+    elif kind == "positive":          # no cancellation
+        draw = lambda: workloads.e4m3_codes(np.abs(workloads.normal(rng, shape)) * np.float32(32.0))
+    elif kind == "uniform_codes":     # every finite code equally likely
+        fin = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+        draw = lambda: fin[rng.integers(0, fin.size, shape)]
+    elif kind == "log_uniform":       # magnitudes 2^-9 .. 2^8.8, random signs
+        def draw():
+            mag = np.exp2(rng.uniform(-9.0, 8.8, shape)).astype(np.float32)
+            sign = np.where(rng.random(shape) < 0.5, -1.0, 1.0).astype(np.float32)
+            return workloads.e4m3_codes(mag * sign)
+    elif kind == "dominant":          # one large product among small ones
+        def draw():
+            c = workloads.e4m3_codes(workloads.normal(rng, shape) * np.float32(0.01))
+            c[:, :, 5] = 0x7E
+            return c
+    else:                             # small integers: every sum exact in fp32
+        vals = np.array([0x00, 0x38, 0x40, 0x48, 0xB8, 0xC0, 0xC8], dtype=np.uint8)
+        draw = lambda: vals[rng.integers(0, vals.size, shape)]
+    return draw(), draw()
+
+
+def _probe(x, y, ninstr):
+    import mfma_probe
+    lib = mfma_probe.load()
+    n = x.shape[0]
+    xd, yd = to_dev(x), to_dev(y)
+    out = torch.full((n, 32, 32), float("nan"), dtype=torch.float32, device="cuda")
+    assert lib.mfma_probe_e4m3(xd.data_ptr(), yd.data_ptr(), out.data_ptr(), n, ninstr,
+                               None) == 0
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("kind", ["workload", "positive", "uniform_codes", "log_uniform",
+                                  "dominant", "small_int"])
+def test_mfma_block_error_bound(kind):
+    """One 128-wide K block of the GEMM (two chained instructions from a
+    zero accumulator) and one instruction alone: |hardware - exact| <=
+    C_MFMA * max_k |x_k y_k| for every output of 1024 tiles; small-integer
+    operands (all partial sums exact in fp32) must give exact sums, which
+    also pins the probe's lane layout."""
+    n = 1024
+    announce(f"mfma block error bound, class {kind}, {n} tiles")
+    rng = np.random.default_rng(["workload", "positive", "uniform_codes", "log_uniform",
+                                 "dominant", "small_int"].index(kind) + 9100)
+    x, y = _probe_tiles(kind, n, rng)
+    tab = oracle.e4m3_table()
+    for ninstr in (2, 1):
+        K = 64 * ninstr
+        X, Y = tab[x[:, :, :K]], tab[y[:, :, :K]]
+        exact = np.einsum("nik,njk->nij", X, Y)          # exact: <= 51 significant bits
+        mx = np.concatenate([np.max(np.abs(X[i:i + 64])[:, :, None, :]
+                                    * np.abs(Y[i:i + 64])[:, None, :, :], axis=3)
+                             for i in range(0, n, 64)])
+        err = np.abs(_probe(x, y, ninstr) - exact)
+        assert np.all(np.isfinite(err)), "unwritten probe outputs"
+        if kind == "small_int":
+            assert np.all(err == 0.0), f"{np.sum(err != 0)} inexact small-integer sums"
+            continue
+        ratio = float(np.max(err / mx))
+        announce(f"  {ninstr} instruction(s): max |err| / max|product| = 2^{np.log2(ratio):.2f}")
+        assert ratio <= C_MFMA, f"block error 2^{np.log2(ratio):.2f} above the bound"
 
 
 def pack_reference(w):
@@ -153,8 +254,9 @@ def test_gemm_gated_act(fr, case):
     q_g, s_g = run_gemm(fr, inp, act)
     q_o, s_o, _ = oracle.gemm_gated_act_fp8(inp["a"], inp["a_scales"], inp["w"],
                                             inp["w_scales"], act)
-    ident, rel = check_gemm_interval(q_g, s_g, q_o, s_o, inp, act)
-    announce(f"  fp8 identical {ident:.6f}, scale max rel err {rel:.2e}")
+    ident, single, rel = check_gemm_interval(q_g, s_g, q_o, s_o, inp, act)
+    announce(f"  fp8 identical {ident:.6f} (single-code intervals {single:.6f}), "
+             f"scale max rel err {rel:.2e}")
 
 
 def test_gemm_bench_shapes(fr):
@@ -178,8 +280,10 @@ def test_gemm_bench_shapes(fr):
            "w": inp["w"], "w_scales": inp["w_scales"]}
     q_o, s_o, _ = oracle.gemm_gated_act_fp8(sub["a"], sub["a_scales"], sub["w"],
                                             sub["w_scales"], oracle.ACT_SWIGLU)
-    ident, rel = check_gemm_interval(q_g[rows], s_g[rows], q_o, s_o, sub, oracle.ACT_SWIGLU)
-    announce(f"  sampled rows {len(rows)}: fp8 identical {ident:.6f}, scale max rel err {rel:.2e}")
+    ident, single, rel = check_gemm_interval(q_g[rows], s_g[rows], q_o, s_o, sub,
+                                             oracle.ACT_SWIGLU)
+    announce(f"  sampled rows {len(rows)}: fp8 identical {ident:.6f} (single-code "
+             f"{single:.6f}), scale max rel err {rel:.2e}")
 
 
 def test_gemm_large_batch_tile_ragged(fr):
@@ -198,8 +302,9 @@ def test_gemm_large_batch_tile_ragged(fr):
                "w": inp["w"], "w_scales": inp["w_scales"]}
         q_o, s_o, _ = oracle.gemm_gated_act_fp8(sub["a"], sub["a_scales"], sub["w"],
                                                 sub["w_scales"], act)
-        ident, rel = check_gemm_interval(q_g[rows], s_g[rows], q_o, s_o, sub, act)
-        announce(f"  act {act}: sampled rows {len(rows)}: fp8 identical {ident:.6f}")
+        ident, single, rel = check_gemm_interval(q_g[rows], s_g[rows], q_o, s_o, sub, act)
+        announce(f"  act {act}: sampled rows {len(rows)}: fp8 identical {ident:.6f} "
+                 f"(single-code {single:.6f})")
 
 
 def test_gemm_worked_example(fr):
