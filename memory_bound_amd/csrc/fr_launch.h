@@ -55,6 +55,8 @@ struct QkvArgs {
     float eps;
     float theta;
     float q_scale;          // multiplies Q after RoPE
+    double l2t;             // -2 log2(theta) / D: set by launch_qkv
+    float inv_d;            // 1 / D: set by launch_qkv
 };
 
 // Gated activation on interleaved gate/up + block-128 FP8.

@@ -69,16 +69,16 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     __shared__ float red_max[8];
 
     const int lane = threadIdx.x & 63;
-    // Wave in the workgroup and row in the workgroup.  For the plain and
-    // LayerNorm modes they are made uniform (readfirstlane), so the row
-    // arithmetic runs on the scalar unit and the division is skipped for
-    // the launch shapes (one row per workgroup, or one wave per row); that
-    // takes ~80 vector instructions off op (a)'s ~580 per wave (measured
-    // 1.4% faster at 8192 x 4096).  The adaptive op, at the ceiling of its
-    // access pattern, keeps the vector form (no gain measured).
-    const int wave = ADA ? (int)(threadIdx.x >> 6)
-                         : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int rw = ADA ? wave / a.nw : (a.nw == 1 ? wave : (a.rpb == 1 ? 0 : wave / a.nw));
+    // Wave in the workgroup and row in the workgroup, made uniform
+    // (readfirstlane), so the row arithmetic runs on the scalar unit, the
+    // loads use scalar-base addressing and the division is skipped for the
+    // launch shapes (one row per workgroup, or one wave per row).  That takes
+    // ~80 vector instructions off op (a)'s ~580 per wave (1.4% faster at
+    // 8192 x 4096), and brings the adaptive op from 70 to 57 registers, so
+    // 8 instead of 7 waves fit per SIMD (8192 x 1024 fp16: one round of
+    // 8192 waves instead of 1.14; 2% faster at 4096 tokens, 0-1% at 8192).
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int rw = a.nw == 1 ? wave : (a.rpb == 1 ? 0 : wave / a.nw);
     const int ww = wave - rw * a.nw;                     // wave in the row
     const int64_t t_row = (int64_t)blockIdx.x * a.rpb + rw;
     const bool row_ok = t_row < a.T;

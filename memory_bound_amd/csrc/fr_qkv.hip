@@ -12,14 +12,20 @@
 // 16-byte chunk j of the first half of the head and chunk j of the second
 // half, so each rotate-half pair (i, i+D/2) -- and each interleaved pair
 // (2i, 2i+1) -- sits in one lane's registers.  Each group's loads are issued
-// while the previous group is processed.  The per-head sum of squares is a DPP reduction over the LP
-// lanes.  The D/2 rotation angles of the token are shared by every head: the
-// wave computes each of them once (one or two per lane) into a per-wave LDS
-// table, then every lane reads the cos/sin of its own pairs.  Angles are
-// formed in fp64 (pos * theta^(-2i/D), reduced modulo pi/2 by a
-// two-constant Cody-Waite step with fma) and sine/cosine come from Taylor
-// polynomials on [-pi/4, pi/4], so the angle stays exact to ~1e-16 for any
-// int32 position.
+// while the previous group is processed.  The wave index is uniform
+// (readfirstlane), so the token's position and page-table entry are scalar
+// loads (through the scalar cache, after the first row loads, so their
+// dependent chain does not queue behind them), and the row arithmetic runs
+// on the scalar unit.  The per-head sum of squares is a DPP reduction over
+// the LP lanes, and rstd the hardware reciprocal square root.  The D/2
+// rotation angles of the token are shared by every head: the wave computes
+// each of them once (one or two per lane) into a per-wave LDS table, then
+// every lane reads the cos/sin of its own pairs.  Angles are formed in fp64:
+// theta^(-2i/D) = 2^(i * step) with step = -2 log2(theta) / D computed on
+// the host, times the position, reduced modulo pi/2 by a two-constant
+// Cody-Waite step with fma; sine and cosine come from Taylor polynomials on
+// [-pi/4, pi/4], so the angle stays exact to ~1e-15 for any int32 position.
+// The RoPE layout is a template parameter.
 #include "fr_device.h"
 #include "fr_launch.h"
 
@@ -29,12 +35,12 @@ constexpr int kQkvMaxGroups = 8;   // head groups one wave may take
 
 // NT: non-temporal loads of the packed rows and stores of Q, K and V (used
 // in the bandwidth regime, where nothing is re-read soon).
-template <int DT, int LP, bool NT, bool NTS = NT>
+template <int DT, int LP, bool NT, int STYLE, bool NTS = NT>
 __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
     __shared__ float tab[4][2][128];                     // per-wave cos / sin
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t task = (int64_t)blockIdx.x * 4 + wv;
     if (task >= a.tasks) return;                         // whole wave exits
     const int64_t t = task / a.wpt;                      // token
@@ -47,20 +53,6 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
     const int L = D >> 4;                                // lanes with data per head
     const int j = lane & (LP - 1);
     const int hl = lane / LP;                            // head within a group
-
-    // Token metadata (uniform across the wave).
-    const int pos = a.pos[t];
-    int64_t slot = -1;
-    if (pos >= 0) {
-        const int idx = pos / a.page_size;
-        if (idx < a.table_len) {
-            const int page = a.table[idx];
-            if (page >= 0 && page < a.num_pages)
-                slot = (int64_t)page * a.page_size + pos % a.page_size;
-        }
-    }
-    if (slot < 0 && g0 == 0 && lane == 0 && a.err != nullptr)
-        __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // Head group g of this wave: its chunks are loaded one group ahead of
     // the group being processed.  Every lane loads (lanes past the row's
@@ -85,13 +77,28 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         if (a.kw) { kw0 = ld128((const char*)a.kw + off0); kw1 = ld128((const char*)a.kw + off1); }
     }
 
+    // Token metadata (uniform across the wave), read through the scalar
+    // cache so that its dependent loads do not wait behind the row loads.
+    typedef const __attribute__((address_space(4))) int32_t* cptr;
+    const int pos = *((cptr)(uintptr_t)a.pos + t);
+    int64_t slot = -1;
+    if (pos >= 0) {
+        const int idx = pos / a.page_size;
+        if (idx < a.table_len) {
+            const int page = *((cptr)(uintptr_t)a.table + idx);
+            if (page >= 0 && page < a.num_pages)
+                slot = (int64_t)page * a.page_size + pos % a.page_size;
+        }
+    }
+    if (slot < 0 && g0 == 0 && lane == 0 && a.err != nullptr)
+        __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
     // cos/sin table of the token: angle i = pos * theta^(-2i/D), i < D/2.
     float* cs_tab = tab[wv][0];
     float* sn_tab = tab[wv][1];
     {
-        const double l2t = log2((double)a.theta);
         for (int i = lane; i < (D >> 1); i += 64) {
-            const double f = exp2(-(double)(2 * i) / (double)D * l2t);
+            const double f = exp2((double)i * a.l2t);
             float sv, cv;
             sincos_pos((double)pos * f, &sv, &cv);
             cs_tab[i] = cv;
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
     if (j < L) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int i = a.style == 0 ? 8 * j + e
+            const int i = STYLE == 0 ? 8 * j + e
                                        : (e < 4 ? 4 * j + e : (D >> 2) + 4 * j + (e - 4));
             cs[e] = cs_tab[i];
             sn[e] = sn_tab[i];
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         const bool has_norm = !is_v && (is_q ? a.qw : a.kw) != nullptr;
         if (has_norm) {
             const u32x4 w0 = is_q ? qw0 : kw0, w1 = is_q ? qw1 : kw1;
-            const float rstd = 1.0f / sqrtf(ss / (float)D + a.eps);
+            const float rstd = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_d, a.eps));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 v[2 * e] = v[2 * e] * rstd * lo16<DT>(w0[e]);
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         }
         if (!active || is_v) return;
 
-        if (a.style == 0) {
+        if constexpr (STYLE == 0) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float x0 = v[e], x1 = v[8 + e];
@@ -188,9 +195,11 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         }
 
         // attention's Q pre-scale (exact for K: a multiply by 1)
-        const float qs = is_q ? a.q_scale : 1.0f;
+        if (a.q_scale != 1.0f) {                         // uniform
+            const float qs = is_q ? a.q_scale : 1.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] *= qs;
+            for (int e = 0; e < 16; ++e) v[e] *= qs;
+        }
 
         u32x4 o0, o1;
 #pragma unroll
@@ -223,16 +232,20 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
     process(ng - 1, n0, n1);
 }
 
+template <int DT, bool NT, int STYLE>
+static const void* pick_qkv(int lp) {
+    switch (lp) {
+    case 1: return (const void*)k_qkv<DT, 1, NT, STYLE>;
+    case 2: return (const void*)k_qkv<DT, 2, NT, STYLE>;
+    case 4: return (const void*)k_qkv<DT, 4, NT, STYLE>;
+    case 8: return (const void*)k_qkv<DT, 8, NT, STYLE>;
+    default: return (const void*)k_qkv<DT, 16, NT, STYLE>;
+    }
+}
+
 template <int DT, bool NT>
 static hipError_t launch_qkv_dt(const QkvArgs& a, int lp, hipStream_t s) {
-    const void* fn;
-    switch (lp) {
-    case 1: fn = (const void*)k_qkv<DT, 1, NT>; break;
-    case 2: fn = (const void*)k_qkv<DT, 2, NT>; break;
-    case 4: fn = (const void*)k_qkv<DT, 4, NT>; break;
-    case 8: fn = (const void*)k_qkv<DT, 8, NT>; break;
-    default: fn = (const void*)k_qkv<DT, 16, NT>; break;
-    }
+    const void* fn = a.style == 0 ? pick_qkv<DT, NT, 0>(lp) : pick_qkv<DT, NT, 1>(lp);
     QkvArgs copy = a;
     void* args[] = {&copy};
     const unsigned blocks = (unsigned)((a.tasks + 3) / 4);
@@ -243,11 +256,15 @@ static hipError_t launch_qkv_dt(const QkvArgs& a, int lp, hipStream_t s) {
 // are split over two waves, so each wave's angles serve several groups and
 // consecutive groups' loads overlap, with non-temporal streaming; measured
 // on MI355X at T = 8192 (32/8 heads x 128, 6 groups): 3 groups per wave
-// ~69% of 8 TB/s, 6 per wave 67%, 1 or 2 per wave 50-58%, and without
-// non-temporal access ~51%.  Small batches give each group its own wave,
+// 68-69% of 8 TB/s, 2 per wave 66%, 1 or 6 per wave 60%; cacheable stores
+// 63%.  A kernel with this op's loads and stores and no arithmetic reaches
+// 72.5% at 8192 tokens and 67% at 4096 (the same bytes as one plain copy
+// stream: 77% and 71%).  Small batches give each group its own wave,
 // trading repeated angle work for parallelism, and keep outputs cacheable.
 hipError_t launch_qkv(const QkvArgs& in, int dtype, hipStream_t s) {
     QkvArgs a = in;
+    a.l2t = -2.0 * log2((double)a.theta) / (double)a.D;   // exponent step per pair
+    a.inv_d = 1.0f / (float)a.D;
     const int L = a.D / 16;
     int lp = 1;
     while (lp < L) lp *= 2;
