@@ -9,9 +9,13 @@ One step = one pass of the whole hot path over one batch of 8192 tokens:
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 `value` is the step's algorithmic bytes over its time (GB/s).  The line also
 carries per-op microseconds, the roofline of the dominant kernel (measured
-with HIP events on the launch stream), the 10-token decoder chain
-(18 layers x 10 steps x 2 ops) replayed as one HIP graph, and the CPU oracle
-timed on a bounded sample of the same workload.
+with HIP events on the launch stream), a sweep of every op over 10 ... 8192
+tokens with a plain streaming copy of the same traffic beside it, the
+Qwen3-style prefill QKV and gated-activation configurations, the 10-token
+decoder chain (18 layers x 10 steps x 2 ops) replayed as one HIP graph and as
+one persistent kernel, the fused gate_up GEMM, the FP4 producers, and the
+CPU oracle timed on a bounded sample of the same workload (one thread and
+all threads).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -36,12 +40,25 @@ T_BIG = 8192
 # (the activation kernel 86-94 us instead of 80-81 us), so an idle spin as
 # head start would time the clock ramp instead of the kernels.
 LEAD_COPIES = 100            # 1 GiB device copies (~0.33 ms each)
+LEAD_BYTES = 1 << 30
+# Buffer rotation: every op's launches cycle through at least this many bytes
+# of distinct buffers (the last-level cache holds 256 MB), the GEMM's weight
+# copies through WEIGHT_ROTATION_BYTES; copies for the achievable figures
+# move COPY_BYTES each way.
+ROTATION_BYTES = 512 << 20
+WEIGHT_ROTATION_BYTES = 400 << 20
+COPY_BYTES = 1 << 30
 _LEAD = {}
+
+
+def progress(msg):
+    """One line per benchmark leg on stderr, before its GPU work starts."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def lead_in(torch, stream):
     if "src" not in _LEAD:
-        _LEAD["src"] = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+        _LEAD["src"] = torch.zeros(LEAD_BYTES, dtype=torch.uint8, device="cuda")
         _LEAD["dst"] = torch.empty_like(_LEAD["src"])
     with torch.cuda.stream(stream):
         for _ in range(LEAD_COPIES):
@@ -52,10 +69,10 @@ GROUP_REPEATS = 3
 EPS = 1e-6
 
 
-def op_bytes():
-    """Algorithmic HBM bytes per call (each input read once, each output
-    written once; 16-bit values 2 B, FP8 1 B, fp32 scales 4 B, int32 4 B)."""
-    T = T_BIG
+def op_bytes(T=T_BIG):
+    """Algorithmic HBM bytes per call at T tokens (each input read once, each
+    output written once; 16-bit values 2 B, FP8 1 B, fp32 scales 4 B, int32
+    4 B; page-table entries: one per 16-token page touched)."""
     H_a, H_ada = 4096, 1024
     Hq, Hkv, D, P = 32, 8, 128, 16
     I = 12288
@@ -66,7 +83,7 @@ def op_bytes():
         "adarms_gate_res_fp8": T * H_ada * (5 * 2 + 2 + 1),
         # qkv in; q_out + k + v out; positions; page-table entries; 2 norm weights
         "qkv_normrope_kvwrite": 2 * T * (Hq + 2 * Hkv) * D * 2 + 4 * T
-        + 4 * (T // P) + 2 * D * 2,
+        + 4 * (-(-T // P)) + 2 * D * 2,
         # gate_up in; fp8 out; block scales
         "gated_act_fp8": T * 2 * I * 2 + T * I + 4 * T * (I // 128),
     }
@@ -132,12 +149,13 @@ def main():
     def sets(d, nbytes_op):
         if args.pmc_pass:
             return [d]
-        r = max(2, -(-(512 << 20) // nbytes_op))
+        r = max(2, -(-ROTATION_BYTES // nbytes_op))
         out = [d]
         for _ in range(r - 1):
             out.append({k: (v.clone() if v is not None else None) for k, v in d.items()})
         return out
 
+    progress("inputs")
     nbytes = op_bytes()
     ri = workloads.resid_rmsnorm_inputs(T, 4096, workloads.BF16, 105, outliers=True)
     A = {k: dev(v) for k, v in ri.items()}
@@ -168,30 +186,39 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    def op_a(i):
-        d = A[i % len(A)]
-        fr.fr_resid_rmsnorm_fp8(d["x"], d["residual"], d["ro"], d["weight"],
-                                fr.W_MUL, EPS, d["q"], fr.Q_TOKEN, 0.0, d["sc"],
-                                T, 4096, fr.BF16, stream=stream)
+    # Each op takes (launch index i, tokens n).  Below 8192 tokens a launch
+    # uses one block of n rows of one buffer set, rotating over every (set,
+    # block) pair, so the rotation spans the same >= 512 MB at every n.
+    def pick(sets_, i, n):
+        stride = -(-n // 16) * 16            # blocks start at multiples of 16 rows (aligned)
+        nb = max(1, T // stride)
+        k = i % (len(sets_) * nb)
+        return sets_[k % len(sets_)], (k // len(sets_)) % nb * stride
 
-    def op_ada(i):
-        d = Ad[i % len(Ad)]
-        fr.fr_adarms_gate_res_fp8(d["x"], d["gate"], d["residual"], d["ro"],
-                                  d["ada_scale"], d["ada_shift"], EPS, d["q"],
-                                  fr.Q_STATIC, 56.0, None, T, 1024, fr.F16,
+    def op_a(i, n=T):
+        d, r = pick(A, i, n)
+        fr.fr_resid_rmsnorm_fp8(d["x"][r:], d["residual"][r:], d["ro"][r:], d["weight"],
+                                fr.W_MUL, EPS, d["q"][r:], fr.Q_TOKEN, 0.0, d["sc"][r:],
+                                n, 4096, fr.BF16, stream=stream)
+
+    def op_ada(i, n=T):
+        d, r = pick(Ad, i, n)
+        fr.fr_adarms_gate_res_fp8(d["x"][r:], d["gate"][r:], d["residual"][r:], d["ro"][r:],
+                                  d["ada_scale"][r:], d["ada_shift"][r:], EPS, d["q"][r:],
+                                  fr.Q_STATIC, 56.0, None, n, 1024, fr.F16,
                                   stream=stream)
 
-    def op_b(i):
-        d = B[i % len(B)]
-        fr.fr_qkv_normrope_kvwrite(d["qkv"], d["q_norm_w"], d["k_norm_w"], EPS,
-                                   d["positions"], 1e6, fr.ROPE_HALF, d["q_out"],
+    def op_b(i, n=T):
+        d, r = pick(B, i, n)
+        fr.fr_qkv_normrope_kvwrite(d["qkv"][r:], d["q_norm_w"], d["k_norm_w"], EPS,
+                                   d["positions"][r:], 1e6, fr.ROPE_HALF, d["q_out"][r:],
                                    d["k_cache"], d["v_cache"], d["page_table"],
-                                   512, 16, 512, d["err"], T, 32, 8, 128,
+                                   512, 16, 512, d["err"], n, 32, 8, 128,
                                    fr.BF16, stream=stream)
 
-    def op_c(i):
-        d = C[i % len(C)]
-        fr.fr_gated_act_fp8(d["gu"], fr.ACT_SWIGLU, d["q"], d["sc"], T, 12288,
+    def op_c(i, n=T):
+        d, r = pick(C, i, n)
+        fr.fr_gated_act_fp8(d["gu"][r:], fr.ACT_SWIGLU, d["q"][r:], d["sc"][r:], n, 12288,
                             fr.BF16, stream=stream)
 
     ops = [("resid_rmsnorm_fp8", op_a), ("adarms_gate_res_fp8", op_ada),
@@ -201,7 +228,7 @@ def main():
     if args.pmc_pass:
         # calibration copy of known size (1 GiB read + 1 GiB written), then
         # each op three times
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         with torch.cuda.stream(stream):
             for _ in range(3):
@@ -214,13 +241,14 @@ def main():
         run_qknorm(torch, fr, workloads, dev, stream, 3, timed=False, only="wan")
         run_gemm_act(torch, fr, workloads, dev, stream, reps=3, timed=False,
                      shapes=((128, 2048, 6144),))
-        print(json.dumps({"pmc_pass": True, "copy_bytes_each_way": 1 << 30,
+        print(json.dumps({"pmc_pass": True, "copy_bytes_each_way": COPY_BYTES,
                           "op_bytes": nbytes}), flush=True)
         return
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    progress("timed step region")
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             for _, f in ops:
@@ -293,22 +321,41 @@ def main():
         "avg_launch_us": dom_us,
     }
 
+    progress("decoder chain (graph + persistent)")
     # ---- 10-token decoder chain: 18 layers x 10 steps, one HIP graph -----
     chain = run_chain(torch, fr, workloads, HipGraph, dev, stream,
                       args.chain_replays)
 
+    progress("10-token standalone calls")
     # ---- standalone 10-token decode-boundary calls (median of 50) --------
     small = run_small(torch, fr, workloads, dev, stream)
 
+    progress("fused gate_up GEMM")
     # ---- gate_up FP8 GEMM fused with SwiGLU + block-128 FP8 --------------
     gemm = run_gemm_act(torch, fr, workloads, dev, stream)
 
+    progress("MX FP4 producers")
     # ---- MX FP4 producers at 8192 tokens ---------------------------------
     mxfp4 = run_mxfp4(torch, fr, workloads, dev, stream, args.steps)
 
+    progress("Q/K norm + RoPE variants")
     # ---- Q/K norm + RoPE variants at 8192 tokens -------------------------
     qknorm = run_qknorm(torch, fr, workloads, dev, stream, args.steps)
 
+    progress("T sweep")
+    # ---- T sweep of the four ops, with the plain-copy reference ---------
+    support = load_support()
+    sweep = run_t_sweep(torch, stream, dict(ops), support, args.steps)
+
+    progress("configurations")
+    # ---- the pages' other configurations (Qwen3 prefill QKV, gated act) --
+    configs = run_configs(torch, fr, workloads, dev, stream)
+
+    progress("achievable copies")
+    # ---- achievable: plain copies of COPY_BYTES each way ------------------
+    achievable = run_achievable(torch, stream, support)
+
+    progress("CPU oracle baseline")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_seconds)
@@ -343,10 +390,207 @@ def main():
         "gemm_gated_act_fp8": gemm,
         "mxfp4_producers": mxfp4,
         "qk_norm_rope_variants": qknorm,
+        "t_sweep": sweep,
+        "configs": configs,
+        "achievable": achievable,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+T_SWEEP = (10, 128, 1024, 4096, 8192)
+SWEEP_GROUPS = 7
+
+
+def load_support():
+    """The measurement support library (tests/gpu_support.hip, built by
+    __graft_entry__.build()): its plain streaming copy is the reference for
+    what a kernel moving the same bytes reaches on this GPU."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_gpu_support", os.path.join(HERE, "tests", "gpu_support.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.load()
+
+
+def pct(v, q):
+    return round(float(np.percentile(v, q)), 3)
+
+
+def time_groups(torch, stream, f, launches, groups, lead=True):
+    """Per-launch microseconds of `groups` groups of `launches` back-to-back
+    launches f(i), each group after the lead-in, events at the group ends."""
+    out = []
+    for _ in range(groups):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        if lead:
+            lead_in(torch, stream)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for i in range(launches):
+                f(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / launches)
+    return out
+
+
+def time_standalone(torch, stream, f, calls=50):
+    """Per-call microseconds of single launches, each bracketed by events and
+    synchronised (launch latency included)."""
+    ts = []
+    for i in range(calls + 5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        f(i)
+        e1.record(stream)
+        stream.synchronize()
+        if i >= 5:
+            ts.append(e0.elapsed_time(e1) * 1e3)
+    return ts
+
+
+_COPY_BUFS = {}
+
+
+def copy_reference(torch, stream, support, nbytes, groups=SWEEP_GROUPS, launches=20):
+    """The plain streaming copy moving `nbytes` of traffic (nbytes / 2 read,
+    nbytes / 2 written), non-temporal and cacheable, buffers rotated through
+    >= 512 MB; returns the faster one's median per-launch microseconds."""
+    half = (nbytes // 2) // 16 * 16
+    if "buf" not in _COPY_BUFS:
+        _COPY_BUFS["buf"] = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    buf = _COPY_BUFS["buf"]
+    buf_bytes = buf.numel()
+    assert 2 * half <= buf_bytes, "copy reference larger than its buffer"
+    nset = max(1, min(buf_bytes // (2 * max(half, 1)), 64))   # source / dest pairs
+    base = buf.data_ptr()
+    best = None
+    for nt in (1, 0):
+        def f(i, nt=nt):
+            k = i % nset
+            rc = support.stream_copy(base + 2 * k * half, base + (2 * k + 1) * half,
+                                     half // 16, nt, stream.cuda_stream)
+            assert rc == 0, rc
+        f(0)
+        us = float(np.median(time_groups(torch, stream, f, launches, max(3, groups // 2))))
+        best = us if best is None else min(best, us)
+    return best
+
+
+def run_t_sweep(torch, stream, ops, support, steps):
+    """Each op at T in {10, 128, 1024, 4096, 8192}: p10/p50/p90 over groups of
+    back-to-back launches (per-launch average; each group after the lead-in,
+    so the host has enqueued the group before the GPU reaches it),
+    algorithmic GB/s, fraction of the 8 TB/s peak, and for T >= 1024 the
+    plain streaming copy of the same traffic as the achievable reference.
+    At T <= 128 the time is launch and latency, reported in microseconds
+    (and single calls' medians, which include the host's launch cost)."""
+    out = {}
+    for name, f in ops.items():
+        out[name] = {}
+        for n in T_SWEEP:
+            progress(f"  {name} T={n}")
+            nb = op_bytes(n)[name]
+            g = lambda i, n=n, f=f: f(i, n)
+            g(0)
+            us = time_groups(torch, stream, g, steps, SWEEP_GROUPS)
+            p50 = float(np.median(us))
+            e = {"bytes": nb, "us_p10": pct(us, 10), "us_p50": pct(us, 50),
+                 "us_p90": pct(us, 90),
+                 "GBps": round(nb / (p50 * 1e-6) / 1e9, 1),
+                 "frac_of_peak": round(nb / (p50 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            if n >= 1024:
+                cu = copy_reference(torch, stream, support, nb)
+                e["copy_same_bytes_us"] = round(cu, 3)
+                e["copy_same_bytes_frac_of_peak"] = round(nb / (cu * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+                e["frac_of_copy"] = round(cu / p50, 4)
+            else:
+                st = time_standalone(torch, stream, g)
+                e["standalone_us_p50"] = pct(st, 50)
+            out[name][f"T{n}"] = e
+    return out
+
+
+def run_configs(torch, fr, workloads, dev, stream):
+    """The Qwen3-style prefill QKV post-processing (S = 128, 32/8 heads x
+    128 bf16, theta 1e6, 16-token pages, 512 pages, permuted table) and the
+    gated activation with block-128 FP8 on [S, 2 x 6144] bf16 for S in
+    {128, 192, 1024}, SwiGLU and GeGLU: per-call microseconds (single calls,
+    p10/p50/p90 of 50) and back-to-back per-launch microseconds (p10/p50/p90
+    over 7 groups), with algorithmic GB/s."""
+    out = {}
+    # every closure below binds its sizes and buffers as default arguments
+    # (a free variable would be read at call time)
+    Sq = 128
+    qi = workloads.qkv_inputs(Sq, 32, 8, 128, workloads.BF16, 103, page_size=16,
+                              num_pages=512)
+    dq = {k: dev(v) for k, v in qi.items()}
+    dq["q_out"] = torch.empty((Sq, 32, 128), dtype=torch.int16, device="cuda")
+    dq["err"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def qkv(i, d=dq, n=Sq):
+        fr.fr_qkv_normrope_kvwrite(d["qkv"], d["q_norm_w"], d["k_norm_w"], EPS,
+                                   d["positions"], 1e6, fr.ROPE_HALF, d["q_out"],
+                                   d["k_cache"], d["v_cache"], d["page_table"], 512,
+                                   16, 512, d["err"], n, 32, 8, 128, fr.BF16,
+                                   stream=stream)
+
+    cases = [("qwen3_prefill_qkv_S128_32x8x128_bf16", qkv,
+              2 * Sq * 48 * 128 * 2 + 4 * Sq + 4 * (Sq // 16) + 2 * 128 * 2)]
+    I = 6144
+    for Sa in (128, 192, 1024):
+        gi = workloads.gated_act_inputs(Sa, I, workloads.BF16, 104)
+        gu = dev(gi["gate_up"])
+        q = torch.empty((Sa, I), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((Sa, I // 128), dtype=torch.float32, device="cuda")
+        for act, an in ((fr.ACT_SWIGLU, "swiglu"), (fr.ACT_GEGLU_TANH, "geglu")):
+            def f(i, gu=gu, q=q, sc=sc, n=Sa, act=act):
+                fr.fr_gated_act_fp8(gu, act, q, sc, n, I, fr.BF16, stream=stream)
+            cases.append((f"gated_act_{an}_S{Sa}_I{I}_bf16", f,
+                          Sa * 2 * I * 2 + Sa * I + 4 * Sa * (I // 128)))
+    for name, f, nb in cases:
+        progress(f"  {name}")
+        f(0)
+        torch.cuda.synchronize()
+        st = time_standalone(torch, stream, f)
+        bb = time_groups(torch, stream, f, 50, SWEEP_GROUPS)
+        out[name] = {"bytes": nb,
+                     "standalone_us_p10": pct(st, 10), "standalone_us_p50": pct(st, 50),
+                     "standalone_us_p90": pct(st, 90),
+                     "back_to_back_us_p10": pct(bb, 10), "back_to_back_us_p50": pct(bb, 50),
+                     "back_to_back_us_p90": pct(bb, 90),
+                     "GBps_back_to_back": round(nb / (float(np.median(bb)) * 1e-6) / 1e9, 1)}
+    return out
+
+
+def run_achievable(torch, stream, support):
+    """Plain copies of 1 GiB each way: the runtime's device-to-device copy
+    (hipMemcpyAsync, through torch) and the streaming copy kernel."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+
+    def d2d(i):
+        dst.copy_(src)
+
+    def sc(i, nt):
+        assert support.stream_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES // 16, nt,
+                                   stream.cuda_stream) == 0
+    res = {}
+    for name, f in (("hip_memcpy_d2d", d2d), ("stream_copy_nontemporal", lambda i: sc(i, 1)),
+                    ("stream_copy_cacheable", lambda i: sc(i, 0))):
+        f(0)
+        us = float(np.median(time_groups(torch, stream, f, 5, 3)))
+        res[name + "_GBps"] = round(2 * COPY_BYTES / (us * 1e-6) / 1e9, 1)
+    res["note"] = ("1 GiB read + 1 GiB written per copy; the T sweep gives the "
+                   "streaming copy at each op's own traffic")
+    del src, dst
+    return res
 
 
 def run_chain(torch, fr, workloads, HipGraph, dev, stream, replays):
@@ -449,6 +693,7 @@ def run_gemm_act(torch, fr, workloads, dev, stream, reps=20, timed=True,
     them from HBM."""
     out = {}
     for (M, K, I) in shapes:
+        progress(f"  gemm M={M} K={K} I={I}")
         inp = workloads.gemm_inputs(M, K, I, 800 + M)
         a, a_s = dev(inp["a"]), dev(inp["a_scales"])
         w_raw, w_s = dev(inp["w"]), dev(inp["w_scales"])
@@ -456,7 +701,7 @@ def run_gemm_act(torch, fr, workloads, dev, stream, reps=20, timed=True,
         fr.fr_gemm_pack_weights(w_raw, w0, 2 * I, K, stream=stream)
         torch.cuda.synchronize()
         del w_raw
-        nw = max(2, -(-(400 << 20) // w0.numel())) if timed else 1
+        nw = max(2, -(-WEIGHT_ROTATION_BYTES // w0.numel())) if timed else 1
         ws = [w0] + [w0.clone() for _ in range(nw - 1)]
         q = torch.empty((M, I), dtype=torch.uint8, device="cuda")
         sc = torch.empty((M, I // 128), dtype=torch.float32, device="cuda")
@@ -507,7 +752,7 @@ def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
     N = [{k: dev(v) for k, v in ri.items()}]
     G = [{"gu": dev(gi["gate_up"])}]
     for lst, nb in ((N, nb_norm), (G, nb_act)):
-        for _ in range(max(2, -(-(512 << 20) // nb)) - 1 if timed else 0):
+        for _ in range(max(2, -(-ROTATION_BYTES // nb)) - 1 if timed else 0):
             lst.append({k: v.clone() for k, v in lst[0].items()})
     for d in N:
         d["ro"] = torch.empty_like(d["x"])
@@ -582,7 +827,7 @@ def run_qknorm(torch, fr, workloads, dev, stream, reps, timed=True, only=None):
                                             scope_full=full, rope3=r3, grid=(8, 32, 32))
         w = {k: dev(inp[k]) for k in ("q_norm_w", "q_norm_b", "k_norm_w", "k_norm_b", "positions")}
         sets = []
-        for _ in range(max(2, -(-(512 << 20) // nb)) if timed else 1):
+        for _ in range(max(2, -(-ROTATION_BYTES // nb)) if timed else 1):
             sets.append({"qkv": dev(inp["qkv"]),
                          "q": torch.empty((T, Hq, D), dtype=torch.int16, device="cuda"),
                          "k": torch.empty((T, Hkv, D), dtype=torch.int16, device="cuda"),
@@ -681,54 +926,133 @@ def run_small(torch, fr, workloads, dev, stream):
     return out
 
 
+def cpu_threads():
+    """Host threads this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when that is set (the share of the host given to it)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(budget_s):
-    """The oracle (plain C, double precision, one thread) on a row sample of
-    the same four ops, sized to about `budget_s` seconds; reported in the
-    same unit (algorithmic GB/s)."""
+    """The oracle (plain C, double precision, as written) on row samples of
+    the same four ops, in two settings: one thread, and the rows split over
+    every host thread this process may use (the ops are row-independent, so
+    the split is a harness split, not an oracle change; ctypes releases the
+    GIL during each C call).  Only the C calls are timed (inputs and outputs
+    are allocated before).  Reported in the same unit (algorithmic GB/s),
+    with per-op milliseconds and their extrapolation to the 8192-token call."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     import workloads
+    L = oracle.lib()
+    nthr = cpu_threads()
+    rows1 = {"resid_rmsnorm_fp8": 64, "adarms_gate_res_fp8": 256,
+             "qkv_normrope_kvwrite": 32, "gated_act_fp8": 16}
+    R = {k: v * nthr for k, v in rows1.items()}
+    ri = workloads.resid_rmsnorm_inputs(R["resid_rmsnorm_fp8"], 4096, workloads.BF16, 105,
+                                        outliers=True)
+    ai = workloads.adarms_inputs(R["adarms_gate_res_fp8"], 1024, workloads.F16, 102)
+    qi = workloads.qkv_inputs(R["qkv_normrope_kvwrite"], 32, 8, 128, workloads.BF16, 103,
+                              page_size=16, num_pages=512)
+    gi = workloads.gated_act_inputs(R["gated_act_fp8"], 12288, workloads.BF16, 105,
+                                    outliers=True)
+    ra = {"ro": np.empty_like(ri["x"]), "q": np.empty(ri["x"].shape, np.uint8),
+          "sc": np.empty(ri["x"].shape[0], np.float32)}
+    aa = {"ro": np.empty_like(ai["x"]), "q": np.empty(ai["x"].shape, np.uint8)}
+    qa = {"q_out": np.empty((R["qkv_normrope_kvwrite"], 32, 128), np.uint16),
+          "err": np.zeros(nthr, np.int32)}
+    ga = {"q": np.empty((R["gated_act_fp8"], 12288), np.uint8),
+          "sc": np.empty((R["gated_act_fp8"], 96), np.float32)}
+    P = lambda a, off=0: a.ctypes.data + off
+
+    def run(op, r0, r1, w):
+        n = r1 - r0
+        if op == "resid_rmsnorm_fp8":
+            rb = r0 * 4096 * 2
+            rc = L.oracle_resid_rmsnorm_fp8(
+                P(ri["x"], rb), P(ri["residual"], rb), P(ra["ro"], rb), P(ri["weight"]),
+                oracle.W_MUL, EPS, P(ra["q"], r0 * 4096), oracle.Q_TOKEN, 0.0,
+                P(ra["sc"], r0 * 4), n, 4096, oracle.BF16)
+        elif op == "adarms_gate_res_fp8":
+            rb = r0 * 1024 * 2
+            rc = L.oracle_adarms_gate_res_fp8(
+                P(ai["x"], rb), P(ai["gate"], rb), P(ai["residual"], rb), P(aa["ro"], rb),
+                P(ai["ada_scale"], rb), P(ai["ada_shift"], rb), EPS, P(aa["q"], r0 * 1024),
+                oracle.Q_STATIC, 56.0, None, n, 1024, oracle.F16)
+        elif op == "qkv_normrope_kvwrite":
+            rc = L.oracle_qkv_normrope_kvwrite(
+                P(qi["qkv"], r0 * 48 * 128 * 2), P(qi["q_norm_w"]), P(qi["k_norm_w"]), EPS,
+                P(qi["positions"], r0 * 4), 1e6, oracle.ROPE_HALF, 1.0,
+                P(qa["q_out"], r0 * 32 * 128 * 2), P(qi["k_cache"]), P(qi["v_cache"]),
+                P(qi["page_table"]), 512, 16, 512, P(qa["err"], w * 4), n, 32, 8, 128,
+                oracle.BF16)
+        else:
+            rc = L.oracle_gated_act_fp8(
+                P(gi["gate_up"], r0 * 2 * 12288 * 2), oracle.ACT_SWIGLU,
+                P(ga["q"], r0 * 12288), P(ga["sc"], r0 * 96 * 4), n, 12288, oracle.BF16)
+        assert rc == 0, (op, rc)
+
     nb = op_bytes()
-    # rows per op in the sample, and the fraction of the 8192-token op they are
-    rows = {"resid_rmsnorm_fp8": 64, "adarms_gate_res_fp8": 256,
-            "qkv_normrope_kvwrite": 32, "gated_act_fp8": 16}
-    ri = workloads.resid_rmsnorm_inputs(rows["resid_rmsnorm_fp8"], 4096,
-                                        workloads.BF16, 105, outliers=True)
-    ai = workloads.adarms_inputs(rows["adarms_gate_res_fp8"], 1024, workloads.F16, 102)
-    qi = workloads.qkv_inputs(rows["qkv_normrope_kvwrite"], 32, 8, 128,
-                              workloads.BF16, 103, page_size=16, num_pages=512)
-    gi = workloads.gated_act_inputs(rows["gated_act_fp8"], 12288, workloads.BF16,
-                                    105, outliers=True)
-    oracle.lib()
+    ops = list(rows1)
 
-    def one_pass():
-        oracle.resid_rmsnorm_fp8(ri["x"], ri["residual"], ri["weight"],
-                                 oracle.W_MUL, EPS, oracle.Q_TOKEN, 0.0, oracle.BF16)
-        oracle.adarms_gate_res_fp8(ai["x"], ai["gate"], ai["residual"],
-                                   ai["ada_scale"], ai["ada_shift"], EPS,
-                                   oracle.Q_STATIC, 56.0, oracle.F16)
-        oracle.qkv_normrope_kvwrite(qi["qkv"], qi["q_norm_w"], qi["k_norm_w"], EPS,
-                                    qi["positions"], 1e6, oracle.ROPE_HALF,
-                                    qi["k_cache"], qi["v_cache"], qi["page_table"],
-                                    16, 32, 8, 128, oracle.BF16)
-        oracle.gated_act_fp8(gi["gate_up"], oracle.ACT_SWIGLU, oracle.BF16)
+    def setting(nt, seconds):
+        pool = ThreadPoolExecutor(nt) if nt > 1 else None
+        rows = {k: rows1[k] * nt for k in ops}
+        per_op = {k: 0.0 for k in ops}
+        passes = 0
+        t_end = time.perf_counter() + seconds
+        while passes < 1 or time.perf_counter() < t_end:
+            for op in ops:
+                chunk = rows[op] // nt
+                t0 = time.perf_counter()
+                if pool is None:
+                    run(op, 0, rows[op], 0)
+                else:
+                    list(pool.map(lambda w, op=op: run(op, w * chunk, (w + 1) * chunk, w),
+                                  range(nt)))
+                per_op[op] += time.perf_counter() - t0
+            passes += 1
+        if pool is not None:
+            pool.shutdown()
+        secs = sum(per_op.values()) / passes
+        sample_bytes = sum(nb[k] * rows[k] / T_BIG for k in ops)
+        return {
+            "threads": nt,
+            "GBps": round(sample_bytes / secs / 1e9, 4),
+            "passes": passes,
+            "rows": rows,
+            "ms_per_op_sample": {k: round(v / passes * 1e3, 3) for k, v in per_op.items()},
+            "ms_per_8192_token_call": {k: round(v / passes * 1e3 * T_BIG / rows[k], 1)
+                                       for k, v in per_op.items()},
+        }
 
-    sample_bytes = sum(nb[k] * rows[k] / T_BIG for k in rows)
-    t0 = time.perf_counter()
-    one_pass()
-    t1 = time.perf_counter()
-    passes = max(1, int(budget_s / max(t1 - t0, 1e-3)) - 1)
-    for _ in range(passes):
-        one_pass()
-    t2 = time.perf_counter()
-    secs = (t2 - t0) / (passes + 1)
+    one = setting(1, budget_s / 2)
+    allt = setting(nthr, budget_s / 2) if nthr > 1 else one
     return {
-        "value": round(sample_bytes / secs / 1e9, 4),
+        "value": allt["GBps"],
         "unit": "GB/s",
-        "cores": 1,
+        "cores": allt["threads"],
         "kind": "oracle",
-        "sample": f"{passes + 1} passes over the four ops on row subsets of the "
-                  f"8192-token step ({rows}); {secs * 1e3:.1f} ms per pass",
-        "seconds": round(t2 - t0, 2),
+        "sample": (f"rows of the 8192-token step's four ops ({allt['rows']}), split over "
+                   f"{allt['threads']} threads, {allt['passes']} passes; only the C calls "
+                   f"timed"),
+        "cpu_model": cpu_model(),
+        "all_threads": allt,
+        "single_thread": one,
     }
 
 

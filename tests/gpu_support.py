@@ -1,13 +1,14 @@
-"""Build and load the matrix-instruction probe (tests/mfma_probe.hip), a
-test-support library that runs the fused GEMM's e4m3 instruction on given
-tiles.  Built by ``__graft_entry__.build()`` next to this file."""
+"""Build and load the test and measurement support library
+(tests/gpu_support.hip): the matrix-instruction probe the GEMM parity tests
+use, and the plain streaming copy the benchmark reports as its achievable
+reference.  Built by ``__graft_entry__.build()`` next to this file."""
 import ctypes
 import os
 import subprocess
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(_HERE, "mfma_probe.hip")
-LIB = os.path.join(_HERE, "libmfmaprobe.so")
+SRC = os.path.join(_HERE, "gpu_support.hip")
+LIB = os.path.join(_HERE, "libfrsupport.so")
 
 
 def build():
@@ -30,4 +31,7 @@ def load():
     lib.mfma_probe_e4m3.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_int,
                                                             ctypes.c_void_p]
     lib.mfma_probe_e4m3.restype = ctypes.c_int
+    lib.stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_int,
+                                ctypes.c_void_p]
+    lib.stream_copy.restype = ctypes.c_int
     return lib

@@ -146,8 +146,8 @@ def _probe_tiles(kind, n, rng):
 
 
 def _probe(x, y, ninstr):
-    import mfma_probe
-    lib = mfma_probe.load()
+    import gpu_support
+    lib = gpu_support.load()
     n = x.shape[0]
     xd, yd = to_dev(x), to_dev(y)
     out = torch.full((n, 32, 32), float("nan"), dtype=torch.float32, device="cuda")
