@@ -92,6 +92,11 @@ def lib():
         L.or_mx_scale_code.restype = _INT
         L.or_quant_mxfp4.argtypes = [_P, _I64, _P, _P]
         L.or_quant_mxfp4.restype = None
+        L.or_quant_nvfp4.argtypes = [_P, _I64, _D, _P, _P]
+        L.or_quant_nvfp4.restype = None
+        L.oracle_resid_rmsnorm_nvfp4.argtypes = [
+            _P, _P, _P, _P, _INT, _F, _F, _P, _P, _I64, _I64, _INT]
+        L.oracle_resid_rmsnorm_nvfp4.restype = _INT
         L.oracle_resid_rmsnorm_mxfp4.argtypes = [
             _P, _P, _P, _P, _INT, _F, _P, _P, _I64, _I64, _INT]
         L.oracle_resid_rmsnorm_mxfp4.restype = _INT
@@ -213,6 +218,17 @@ def quant_mxfp4(y):
     packed = np.empty(y.size // 2, dtype=np.uint8)
     scales = np.empty(y.size // 32, dtype=np.uint8)
     lib().or_quant_mxfp4(_ptr(y), y.size, _ptr(packed), _ptr(scales))
+    return packed, scales
+
+
+def quant_nvfp4(y, global_scale):
+    """y: float64 [n], n % 16 == 0 -> (packed uint8 [n/2], E4M3 block scale
+    codes uint8 [n/16])."""
+    y = _c(np.ravel(y), np.float64)
+    assert y.size % 16 == 0
+    packed = np.empty(y.size // 2, dtype=np.uint8)
+    scales = np.empty(y.size // 16, dtype=np.uint8)
+    lib().or_quant_nvfp4(_ptr(y), y.size, float(global_scale), _ptr(packed), _ptr(scales))
     return packed, scales
 
 
@@ -367,6 +383,23 @@ def resid_rmsnorm_mxfp4(x, residual, weight, wmode, eps, dtype):
     rc = lib().oracle_resid_rmsnorm_mxfp4(
         _ptr(x), _ptr(residual), _ptr(ro), _ptr(weight), wmode, eps, _ptr(q),
         _ptr(sc), T, H, dtype)
+    assert rc == 0
+    return ro, q, sc
+
+
+def resid_rmsnorm_nvfp4(x, residual, weight, wmode, eps, global_scale, dtype):
+    """Returns (residual_out uint16 [T,H], out_fp4 uint8 [T,H/2],
+    out_scales uint8 [T,H/16] E4M3 block scale codes)."""
+    x = _c(x, np.uint16)
+    residual = _c(residual, np.uint16)
+    T, H = x.shape
+    weight = _c(weight, np.uint16)
+    ro = np.empty_like(x)
+    q = np.empty((T, H // 2), dtype=np.uint8)
+    sc = np.empty((T, H // 16), dtype=np.uint8)
+    rc = lib().oracle_resid_rmsnorm_nvfp4(
+        _ptr(x), _ptr(residual), _ptr(ro), _ptr(weight), wmode, eps, global_scale,
+        _ptr(q), _ptr(sc), T, H, dtype)
     assert rc == 0
     return ro, q, sc
 

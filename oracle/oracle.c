@@ -383,6 +383,42 @@ void or_quant_mxfp4(const double* y, int64_t n, uint8_t* packed, uint8_t* scales
     }
 }
 
+/* ---- NVFP4 [HY 04 step 5 and 06 census: residual_add_rms_norm_to_nvfp4,
+ * the producer of the FP4 GEMM inputs on that GPU].  The pages name the
+ * format only; the reading taken is its published definition: E2M1
+ * elements (the grid above) in blocks of 16 consecutive values, each block
+ * with a scale stored as an E4M3 code, and one fp32 scale for the whole
+ * tensor, so a value decodes as e2m1(code) * e4m3(block code) * g.  The
+ * block scale maps the block's largest magnitude to 6, the largest E2M1
+ * value: block code = E4M3(amax / (6 g)) (nearest, ties to even,
+ * saturating at 448); element code = E2M1(y / S) with S = e4m3(block
+ * code) * g (nearest, ties to even, saturating at 6, the sign kept).  A
+ * block whose scale code decodes to 0 stores zero codes with the elements'
+ * signs.  g, the dequantisation scale of the tensor, is an input (a
+ * calibrated constant, like the static FP8 multiplier). ---- */
+
+/* Blocks of 16 consecutive values: scales[b] = E4M3 code, two elements per
+ * byte, element 2k in bits 3..0 and 2k+1 in bits 7..4. */
+void or_quant_nvfp4(const double* y, int64_t n, double g, uint8_t* packed,
+                    uint8_t* scales)
+{
+    for (int64_t b = 0; b < n / 16; ++b) {
+        const double* yb = y + b * 16;
+        double amax = 0.0;
+        for (int i = 0; i < 16; ++i)
+            if (fabs(yb[i]) > amax)
+                amax = fabs(yb[i]);
+        uint8_t sc = or_e4m3_encode(amax / (6.0 * g));
+        scales[b] = sc;
+        double S = or_e4m3_decode(sc) * g;      /* exact: 4 x 24 significant bits */
+        for (int i = 0; i < 16; i += 2) {
+            uint8_t lo = S > 0.0 ? or_e2m1_encode(yb[i] / S) : (signbit(yb[i]) ? 8 : 0);
+            uint8_t hi = S > 0.0 ? or_e2m1_encode(yb[i + 1] / S) : (signbit(yb[i + 1]) ? 8 : 0);
+            packed[(b * 16 + i) / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
 /* Paged KV-cache slot of a token position [FP, paged cache]: page
  * page_table[pos / page_size], offset pos % page_size.  -1 when the
  * position, the table entry or the page is out of range. */
@@ -473,6 +509,42 @@ int oracle_resid_rmsnorm_mxfp4(const uint16_t* x, const uint16_t* residual,
         }
         or_rmsnorm(ro, w, wmode, H, (double)eps, y);
         or_quant_mxfp4(y, H, out_fp4 + t * (H / 2), out_scales + t * (H / 32));
+    }
+    free(ro); free(w); free(y);
+    return 0;
+}
+
+/* Residual add + RMSNorm + NVFP4 [HY 04 step 5, 06 census:
+ * residual_add_rms_norm_to_nvfp4]: residual_out and y as in the FP8 op; y
+ * is quantised to NVFP4 with the tensor scale global_scale (out_fp4
+ * [T, H/2], out_scales [T, H/16] E4M3 codes). */
+int oracle_resid_rmsnorm_nvfp4(const uint16_t* x, const uint16_t* residual,
+                               uint16_t* residual_out, const uint16_t* weight,
+                               int wmode, float eps, float global_scale,
+                               uint8_t* out_fp4, uint8_t* out_scales, int64_t T,
+                               int64_t H, int dtype)
+{
+    if (H % 16 != 0 || !(global_scale > 0.0f))
+        return -2;
+    double* ro = malloc(sizeof(double) * (size_t)H);
+    double* w = malloc(sizeof(double) * (size_t)H);
+    double* y = malloc(sizeof(double) * (size_t)H);
+    if (!ro || !w || !y) {
+        free(ro); free(w); free(y);
+        return -1;
+    }
+    for (int64_t j = 0; j < H; ++j)
+        w[j] = (wmode != OR_W_NONE) ? dec16(weight[j], dtype) : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t j = 0; j < H; ++j) {
+            uint16_t b = enc16(dec16(x[t * H + j], dtype) + dec16(residual[t * H + j], dtype),
+                               dtype);
+            residual_out[t * H + j] = b;
+            ro[j] = dec16(b, dtype);
+        }
+        or_rmsnorm(ro, w, wmode, H, (double)eps, y);
+        or_quant_nvfp4(y, H, (double)global_scale, out_fp4 + t * (H / 2),
+                       out_scales + t * (H / 16));
     }
     free(ro); free(w); free(y);
     return 0;

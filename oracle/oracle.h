@@ -73,6 +73,8 @@ uint8_t or_e2m1_encode(double v);            /* RNE, |v| >= 6 -> 6, sign kept */
 int     or_mx_scale_code(double amax);       /* E8M0 code of the MX block scale */
 void    or_quant_mxfp4(const double* y, int64_t n, uint8_t* packed,
                        uint8_t* scales);     /* n % 32 == 0 */
+void    or_quant_nvfp4(const double* y, int64_t n, double global_scale,
+                       uint8_t* packed, uint8_t* scales);  /* n % 16 == 0 */
 int64_t or_kv_slot(int64_t pos, const int32_t* page_table, int32_t table_len,
                    int32_t page_size, int32_t num_pages);
 
@@ -107,6 +109,11 @@ int oracle_resid_rmsnorm_mxfp4(const uint16_t* x, const uint16_t* residual,
                                int wmode, float eps, uint8_t* out_fp4,
                                uint8_t* out_scales, int64_t T, int64_t H,
                                int dtype);
+int oracle_resid_rmsnorm_nvfp4(const uint16_t* x, const uint16_t* residual,
+                               uint16_t* residual_out, const uint16_t* weight,
+                               int wmode, float eps, float global_scale,
+                               uint8_t* out_fp4, uint8_t* out_scales, int64_t T,
+                               int64_t H, int dtype);
 int oracle_resid_layernorm(const uint16_t* x, const uint16_t* residual,
                            uint16_t* residual_out, const uint16_t* weight,
                            const uint16_t* bias, float eps, int out_kind,
