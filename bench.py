@@ -334,7 +334,7 @@ def main():
     # ---- gate_up FP8 GEMM fused with SwiGLU + block-128 FP8 --------------
     gemm = run_gemm_act(torch, fr, workloads, dev, stream)
 
-    progress("MX FP4 producers")
+    progress("FP4 producers (MX and NV)")
     # ---- MX FP4 producers at 8192 tokens ---------------------------------
     mxfp4 = run_mxfp4(torch, fr, workloads, dev, stream, args.steps)
 
@@ -388,7 +388,7 @@ def main():
         "chain": chain,
         "decode_t10": small,
         "gemm_gated_act_fp8": gemm,
-        "mxfp4_producers": mxfp4,
+        "fp4_producers": mxfp4,
         "qk_norm_rope_variants": qknorm,
         "t_sweep": sweep,
         "configs": configs,
@@ -739,13 +739,18 @@ def run_gemm_act(torch, fr, workloads, dev, stream, reps=20, timed=True,
     return out
 
 
+NVFP4_SCALE = 3.7e-2        # tensor dequant scale of the NVFP4 producer (amax ~ 100 / (6 * 448))
+
+
 def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
-    """The two MX FP4 producers at the bandwidth shapes (8192 tokens: RMSNorm
-    H=4096 bf16 with weight, SwiGLU I=12288 bf16), buffers rotated through
-    >= 512 MB; reps launches back to back, events at the ends."""
+    """The FP4 producers at the bandwidth shapes (8192 tokens: RMSNorm
+    H=4096 bf16 with weight -> MXFP4 and -> NVFP4, add + LayerNorm ->
+    MXFP4, SwiGLU I=12288 bf16 -> MXFP4), buffers rotated through >= 512 MB;
+    reps launches back to back, events at the ends."""
     T, H, I = T_BIG, 4096, 12288
     e = 2
     nb_norm = T * H * 3 * e + H * e + T * H // 2 + T * H // 32
+    nb_nv = T * H * 3 * e + H * e + T * H // 2 + T * H // 16
     nb_act = T * 2 * I * e + T * I // 2 + T * I // 32
     ri = workloads.resid_rmsnorm_inputs(T, H, workloads.BF16, 105, outliers=True)
     gi = workloads.gated_act_inputs(T, I, workloads.BF16, 104, outliers=True)
@@ -758,6 +763,7 @@ def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
         d["ro"] = torch.empty_like(d["x"])
         d["q"] = torch.empty((T, H // 2), dtype=torch.uint8, device="cuda")
         d["s"] = torch.empty((T, H // 32), dtype=torch.uint8, device="cuda")
+        d["s16"] = torch.empty((T, H // 16), dtype=torch.uint8, device="cuda")
     for d in G:
         d["q"] = torch.empty((T, I // 2), dtype=torch.uint8, device="cuda")
         d["s"] = torch.empty((T, I // 32), dtype=torch.uint8, device="cuda")
@@ -766,6 +772,12 @@ def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
         d = N[i % len(N)]
         fr.fr_resid_rmsnorm_mxfp4(d["x"], d["residual"], d["ro"], d["weight"],
                                   fr.W_MUL, EPS, d["q"], d["s"], T, H,
+                                  fr.BF16, stream=stream)
+
+    def nv(i):
+        d = N[i % len(N)]
+        fr.fr_resid_rmsnorm_nvfp4(d["x"], d["residual"], d["ro"], d["weight"],
+                                  fr.W_MUL, EPS, NVFP4_SCALE, d["q"], d["s16"], T, H,
                                   fr.BF16, stream=stream)
 
     def act(i):
@@ -784,6 +796,7 @@ def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
 
     out = {}
     for name, f, nb in (("resid_rmsnorm_mxfp4_T8192_H4096", norm, nb_norm),
+                        ("resid_rmsnorm_nvfp4_T8192_H4096", nv, nb_nv),
                         ("gated_act_mxfp4_T8192_I12288", act, nb_act),
                         ("resid_layernorm_mxfp4_T8192_H4096", ln, nb_ln)):
         for i in range(3):

@@ -24,10 +24,12 @@
  *    no infinities.  A torch float8_e4m3fn tensor viewed as uint8 matches.
  *    Values are clamped to +-448 before rounding (saturating), rounding is
  *    to nearest, ties to even.
- *  - Arithmetic is fp32 (the RMSNorm sum of squares is accumulated in
- *    fp64).  A value that an op stores and also consumes (the new residual)
- *    is consumed in its stored, rounded form; every other intermediate stays
- *    in fp32 until its single store.
+ *  - Arithmetic is fp32, except where an entry point says otherwise: the
+ *    row sums of the residual norms (RMSNorm sum of squares; LayerNorm mean
+ *    and variance) are accumulated in fp64, while the per-head Q/K norms of
+ *    the QKV ops sum their D values in fp32.  A value that an op stores and
+ *    also consumes (the new residual) is consumed in its stored, rounded
+ *    form; every other intermediate stays in fp32 until its single store.
  *  - Results are deterministic: no atomics in value paths; repeated calls
  *    on the same inputs give bit-identical outputs.
  *
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FR_ABI_VERSION 1
+#define FR_ABI_VERSION 2   /* 2: fr_resid_rmsnorm_nvfp4 added */
 
 typedef enum {
     FR_OK = 0,
@@ -217,6 +219,35 @@ int fr_resid_rmsnorm_mxfp4(const void* x, const void* residual,
                            int64_t T, int64_t H, int dtype, void* stream);
 
 /*
+ * (a-nvfp4) residual add + RMSNorm + NVFP4 [HY 04 step 5 and 06 census:
+ *   residual_add_rms_norm_to_nvfp4, the residual-RMSNorm producer of the FP4
+ *   GEMM inputs].  The pages name the format only; this follows its
+ *   published definition: blocks of 16 consecutive values of a row share an
+ *   E4M3 scale code (encoded as the FP8 outputs above), the whole tensor a
+ *   caller-given fp32 dequantisation scale g; each value is an E2M1 code as
+ *   in the MX producers, and decodes as e2m1(code) * e4m3(block code) * g.
+ *   block code = E4M3(amax / (6 g)), amax the block's largest magnitude
+ *     (nearest, ties to even, saturating at 448), so the block maximum maps
+ *     to 6; element = E2M1(y / S), S = e4m3(block code) * g (nearest even,
+ *     saturating at 6, sign kept); a block whose code decodes to 0 gets zero
+ *     codes with the values' signs.
+ *   residual_out and y exactly as fr_resid_rmsnorm_fp8 (wmode FR_W_NONE /
+ *   MUL / ONE_PLUS).  Both decisions are taken on the exact y (the block
+ *   scale on a double-precision value of amax / (6 g)).
+ *   global_scale: g > 0, finite (FR_ERR_MODE otherwise), e.g. a calibrated
+ *   tensor amax / (6 * 448).  out_fp4: [T, H/2] bytes (16-byte aligned), two
+ *   codes per byte, the even-indexed value in bits 3..0; out_scales:
+ *   [T, H/16] E4M3 codes (any alignment).  H % 16 == 0, H <= 32768.  x,
+ *   residual, residual_out (may equal residual), weight: as
+ *   fr_resid_rmsnorm_fp8.
+ */
+int fr_resid_rmsnorm_nvfp4(const void* x, const void* residual,
+                           void* residual_out, const void* weight, int wmode,
+                           float eps, float global_scale, uint8_t* out_fp4,
+                           uint8_t* out_scales, int64_t T, int64_t H, int dtype,
+                           void* stream);
+
+/*
  * (a-ln) residual add + LayerNorm + FP8 or MXFP4 [HY 06 census: the ViT
  *   add + LayerNorm FP4 producer; FR 二 table step 1 for the fused FP8 form]
  *
@@ -244,7 +275,8 @@ int fr_resid_layernorm_mxfp4(const void* x, const void* residual,
 /*
  * (c-fp4) gated activation + MXFP4: h = act(g) * u as fr_gated_act_fp8 (fp32
  *   activation), quantised in blocks of 32 outputs.  out_fp4: [T, I/2]
- *   bytes (16-byte aligned); out_scales: [T, I/32] bytes.  I % 128 == 0.
+ *   bytes (16-byte aligned); out_scales: [T, I/32] bytes (4-byte aligned:
+ *   the codes of 4 blocks leave as one 4-byte store).  I % 128 == 0.
  */
 int fr_gated_act_mxfp4(const void* gate_up, int act, uint8_t* out_fp4,
                        uint8_t* out_scales, int64_t T, int64_t I, int dtype,

@@ -59,6 +59,8 @@ _SIGS = {
     "fr_gemm_pack_weights": [_P, _P, _I64, _I64, _P],
     "fr_resid_rmsnorm_mxfp4": [_P, _P, _P, _P, _INT, _F, _P, _P, _I64, _I64,
                                _INT, _P],
+    "fr_resid_rmsnorm_nvfp4": [_P, _P, _P, _P, _INT, _F, _F, _P, _P, _I64, _I64,
+                               _INT, _P],
     "fr_gated_act_mxfp4": [_P, _INT, _P, _P, _I64, _I64, _INT, _P],
     "fr_resid_layernorm_fp8": [_P, _P, _P, _P, _P, _F, _P, _INT, _F, _P, _I64,
                                _I64, _INT, _P],
@@ -180,6 +182,15 @@ def fr_resid_rmsnorm_mxfp4(x, residual, residual_out, weight, wmode, eps,
     _check(lib.fr_resid_rmsnorm_mxfp4(
         _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(weight), wmode, eps,
         _ptr(out_fp4), _ptr(out_scales), T, H, dtype, _stream(stream)))
+
+
+def fr_resid_rmsnorm_nvfp4(x, residual, residual_out, weight, wmode, eps,
+                           global_scale, out_fp4, out_scales, T, H, dtype,
+                           stream=None):
+    _check(lib.fr_resid_rmsnorm_nvfp4(
+        _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(weight), wmode, eps,
+        global_scale, _ptr(out_fp4), _ptr(out_scales), T, H, dtype,
+        _stream(stream)))
 
 
 def fr_gated_act_mxfp4(gate_up, act, out_fp4, out_scales, T, I, dtype,

@@ -21,7 +21,7 @@ struct NormArgs {
     const void* ada_shift;  // [T,H]   (adaptive variant only)
     uint8_t* out;           // [T,H] FP8, or [T,H/2] MX FP4
     float* scales;          // [T]     (FR_Q_TOKEN)
-    uint8_t* mx_scales;     // [T,H/32] E8M0 (MX FP4 output)
+    uint8_t* mx_scales;     // [T,H/32] E8M0 (MX FP4 output) or [T,H/16] E4M3 (NVFP4)
     int64_t T;
     int H;
     int nw;                 // wavefronts per row
@@ -31,6 +31,8 @@ struct NormArgs {
     float eps;
     float static_scale;
     double inv_h;           // 1 / H: set by launch_norm
+    float gscale;           // NVFP4 output: the tensor's fp32 dequantisation scale g
+    double inv6g;           // NVFP4 output: 1 / (6 g), set by launch_norm
 };
 
 // Packed QKV split + per-head norm + RoPE + paged KV write.
@@ -144,7 +146,8 @@ struct QkNormArgs {
 };
 hipError_t launch_qknr(const QkNormArgs& a, int dtype, hipStream_t s);
 
-enum { NORM_FP8 = 0, NORM_ADA_FP8 = 1, NORM_MXFP4 = 2, NORM_LAYER_FP8 = 3, NORM_LAYER_MXFP4 = 4 };
+enum { NORM_FP8 = 0, NORM_ADA_FP8 = 1, NORM_MXFP4 = 2, NORM_LAYER_FP8 = 3, NORM_LAYER_MXFP4 = 4,
+       NORM_NVFP4 = 5 };
 hipError_t launch_norm(const NormArgs& a, int dtype, int kind, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int dtype, hipStream_t s);
 hipError_t launch_act(const ActArgs& a, int dtype, int act, bool mx, hipStream_t s);

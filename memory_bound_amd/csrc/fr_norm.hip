@@ -37,6 +37,12 @@
 // scaling.  Round-to-odd keeps both decisions exact: the exponent of the
 // maximum (a value rounded to odd never lands on a power of two it did not
 // equal) and the E2M1 rounding (24 bits rounded to odd, then to 2).
+//
+// NVFP4 output (plain modes; same report, 04 step 5 and 06: the residual
+// RMSNorm producer writes NVFP4 there): blocks of 16 values = 2 lanes with
+// an E4M3 scale mapping the block maximum to 6 and an fp32 tensor scale g
+// given by the caller; both decisions are taken on exact or double values
+// (details at the code).
 #include "fr_device.h"
 #include "fr_launch.h"
 
@@ -59,7 +65,9 @@ __device__ __forceinline__ void st_out(void* p, u32x2 v) {
 
 // NTL / NTS: non-temporal loads of the streamed inputs / stores of the
 // outputs (the norm weight is re-read by every row and stays cached).
-template <int DT, int CPL, int MODE, bool NTL, bool NTS = NTL, bool MX = false>
+// MX / NV: MX FP4 or NVFP4 output instead of FP8 (plain modes; MX also
+// LayerNorm).
+template <int DT, int CPL, int MODE, bool NTL, bool NTS = NTL, bool MX = false, bool NV = false>
 __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     constexpr bool ADA = MODE == M_ADA;
     constexpr bool LAYER = MODE == M_LAYER;
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
             if (ok[k]) tmax = fmaxf(tmax, cmax);         // one select per chunk
         }
     }
-    const bool token_max = !ADA && !MX && a.qmode == 1;
+    const bool token_max = !ADA && !MX && !NV && a.qmode == 1;
     double ss = wave_sum_d(ss0 + ss1);
     if (token_max) tmax = wave_reduce(tmax, OpMaxMag());
     if (a.nw > 1) {
@@ -325,6 +333,51 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
         }
     } else {
         // Pass 3 (plain): the FP8 / FP4 codes of t * rstd * K.
+        if constexpr (NV) {
+            // NVFP4: a block of 16 values is a lane pair.  The block scale
+            // code is E4M3(amax / (6 g)), decided on the double value
+            // max|t| * rstd / (6 g) (|t| exact: hi + lo in double), rounded
+            // to odd into fp32 before the saturating conversion, so the
+            // conversion rounds the double value.  The elements are the
+            // E2M1 codes of t * (rstd / S), S = e4m3(code) * g exact in
+            // fp64, formed as round-to-odd products like the FP8 path.
+            uint8_t* orow4 = a.out + t * (int64_t)(a.H >> 1);
+            uint8_t* srow = a.mx_scales + t * (int64_t)(a.H >> 4);
+            const double c6 = rstd_d * a.inv6g;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                double m = 0.0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    m = fmax(m, fabs((double)th[k][e] + (double)tl[k][e]));
+                m = fmax(m, dpp_d<DPP_PAIR>(m));         // the block's other lane
+                const double sd = m * c6;
+                const float sh = (float)sd;
+                const float sf = round_odd(sh, (float)(sd - (double)sh));
+                const int code = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(sf), 0.0f, 0, false) & 0xFF;
+                const double S = (double)__builtin_amdgcn_cvt_f32_fp8(code, 0) * (double)a.gscale;
+                const double Kd = S > 0.0 ? rstd_d * rcp_d(S) : 0.0;
+                const float Kh = (float)Kd;
+                const float Kl = (float)(Kd - (double)Kh);
+                float q[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float p = th[k][e] * Kh;
+                    float r = fmaf(th[k][e], Kh, -p);
+                    r = fmaf(th[k][e], Kl, r);
+                    if constexpr (MODE == M_ONE_PLUS) r = fmaf(tl[k][e], Kh, r);
+                    q[e] = round_odd(p, r);
+                }
+                const u32 pk = pack_e2m1x8(q, 1.0f);
+                if (ok[k] && row_ok) {
+                    const int c = k * stride + ww * 64 + lane;
+                    u32* dst = (u32*)(orow4 + c * 4);
+                    if constexpr (NTS) __builtin_nontemporal_store(pk, dst); else *dst = pk;
+                    if ((lane & 1) == 0) srow[c >> 1] = (uint8_t)code;
+                }
+            }
+            return;
+        }
         if constexpr (MX) {
             const float Kh = (float)rstd_d;
             const float Kl = (float)(rstd_d - (double)Kh);
@@ -393,17 +446,17 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
     }
 }
 
-template <int DT, int MODE, bool NT, bool MX>
+template <int DT, int MODE, bool NT, bool MX, bool NV = false>
 static hipError_t launch_norm_mode(const NormArgs& a, int cpl, hipStream_t s) {
     // the adaptive op's outputs are stored cacheable even when streaming
     // (measured 2-3% faster at 8192 x 1024 fp16)
     constexpr bool NTS = NT && MODE != M_ADA;
     const void* fn;
     switch (cpl) {
-    case 1: fn = (const void*)k_norm<DT, 1, MODE, NT, NTS, MX>; break;
-    case 2: fn = (const void*)k_norm<DT, 2, MODE, NT, NTS, MX>; break;
-    case 4: fn = (const void*)k_norm<DT, 4, MODE, NT, NTS, MX>; break;
-    default: fn = (const void*)k_norm<DT, 8, MODE, NT, NTS, MX>; break;
+    case 1: fn = (const void*)k_norm<DT, 1, MODE, NT, NTS, MX, NV>; break;
+    case 2: fn = (const void*)k_norm<DT, 2, MODE, NT, NTS, MX, NV>; break;
+    case 4: fn = (const void*)k_norm<DT, 4, MODE, NT, NTS, MX, NV>; break;
+    default: fn = (const void*)k_norm<DT, 8, MODE, NT, NTS, MX, NV>; break;
     }
     NormArgs copy = a;
     void* args[] = {&copy};
@@ -412,7 +465,15 @@ static hipError_t launch_norm_mode(const NormArgs& a, int cpl, hipStream_t s) {
 }
 
 template <int DT, bool NT>
-static hipError_t launch_norm_dt(const NormArgs& a, int mode, bool mx, int cpl, hipStream_t s) {
+static hipError_t launch_norm_dt(const NormArgs& a, int mode, bool mx, bool nv, int cpl,
+                                 hipStream_t s) {
+    if (nv) {
+        switch (mode) {
+        case M_NONE: return launch_norm_mode<DT, M_NONE, NT, false, true>(a, cpl, s);
+        case M_MUL: return launch_norm_mode<DT, M_MUL, NT, false, true>(a, cpl, s);
+        default: return launch_norm_mode<DT, M_ONE_PLUS, NT, false, true>(a, cpl, s);
+        }
+    }
     if (mx) {
         switch (mode) {
         case M_NONE: return launch_norm_mode<DT, M_NONE, NT, true>(a, cpl, s);
@@ -465,16 +526,18 @@ hipError_t launch_norm(const NormArgs& in, int dtype, int kind, hipStream_t s) {
     const bool adaptive = kind == NORM_ADA_FP8;
     const bool layer = kind == NORM_LAYER_FP8 || kind == NORM_LAYER_MXFP4;
     const bool mx = kind == NORM_MXFP4 || kind == NORM_LAYER_MXFP4;
+    const bool nv = kind == NORM_NVFP4;
     const NormShape sh = pick_norm_shape(a.T, a.H, adaptive);
     a.inv_h = 1.0 / (double)a.H;
+    if (nv) a.inv6g = 1.0 / (6.0 * (double)a.gscale);
     a.nw = sh.nw;
     a.rpb = sh.rpb;
     const int mode = adaptive ? M_ADA : (layer ? M_LAYER : a.wmode);
     if (dtype == DT_BF16)
-        return sh.nt ? launch_norm_dt<DT_BF16, true>(a, mode, mx, sh.cpl, s)
-                     : launch_norm_dt<DT_BF16, false>(a, mode, mx, sh.cpl, s);
-    return sh.nt ? launch_norm_dt<DT_F16, true>(a, mode, mx, sh.cpl, s)
-                 : launch_norm_dt<DT_F16, false>(a, mode, mx, sh.cpl, s);
+        return sh.nt ? launch_norm_dt<DT_BF16, true>(a, mode, mx, nv, sh.cpl, s)
+                     : launch_norm_dt<DT_BF16, false>(a, mode, mx, nv, sh.cpl, s);
+    return sh.nt ? launch_norm_dt<DT_F16, true>(a, mode, mx, nv, sh.cpl, s)
+                 : launch_norm_dt<DT_F16, false>(a, mode, mx, nv, sh.cpl, s);
 }
 
 }  // namespace fr

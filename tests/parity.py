@@ -216,6 +216,19 @@ def run_resid_rmsnorm_mxfp4(fr, inp, wmode, eps, dtype, inplace=False,
     return to_host(ro, np.uint16), to_host(q, np.uint8), to_host(sc, np.uint8)
 
 
+def run_resid_rmsnorm_nvfp4(fr, inp, wmode, eps, gscale, dtype, inplace=False,
+                            poison=0xAA):
+    T, H = inp["x"].shape
+    x, r, w = to_dev(inp["x"]), to_dev(inp["residual"]), to_dev(inp["weight"])
+    ro = r if inplace else torch.full((T, H), POISON16, dtype=torch.int16,
+                                      device="cuda")
+    q = torch.full((T, H // 2), poison, dtype=torch.uint8, device="cuda")
+    sc = torch.full((T, H // 16), 0xFF, dtype=torch.uint8, device="cuda")
+    fr.fr_resid_rmsnorm_nvfp4(x, r, ro, w, wmode, eps, gscale, q, sc, T, H, dtype)
+    torch.cuda.synchronize()
+    return to_host(ro, np.uint16), to_host(q, np.uint8), to_host(sc, np.uint8)
+
+
 def run_gated_act_mxfp4(fr, inp, act, dtype, poison=0xAA):
     T, I2 = inp["gate_up"].shape
     I = I2 // 2

@@ -29,6 +29,7 @@ def test_header_declares_the_four_ops_and_helpers():
         "fr_resid_rmsnorm_fp8", "fr_adarms_gate_res_fp8",
         "fr_qkv_normrope_kvwrite", "fr_gated_act_fp8", "fr_gemm_gated_act_fp8",
         "fr_gemm_pack_weights", "fr_resid_rmsnorm_mxfp4", "fr_gated_act_mxfp4",
+        "fr_resid_rmsnorm_nvfp4",
         "fr_decode_chain_persistent", "fr_qk_norm_rope", "fr_resid_layernorm_fp8",
         "fr_resid_layernorm_mxfp4", "fr_status_string", "fr_abi_version"])
 
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fr.abi_version() == 1
+    assert fr.abi_version() == 2
     for s in range(8):
         assert fr.status_string(s).startswith("FR_")
     assert fr.status_string(99) == "unknown fr_status"
@@ -148,6 +149,31 @@ def test_qkv_validation(kw, status):
     assert qkv(**kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), fr.FR_ERR_NULL),
+    (dict(out_scales=None), fr.FR_ERR_NULL),
+    (dict(wmode=fr.W_MUL, weight=None), fr.FR_ERR_NULL),
+    (dict(out_fp4=E + 4), fr.FR_ERR_ALIGN),
+    (dict(out_scales=F + 1), fr.FR_OK),                         # byte stores: any alignment
+    (dict(H=1032), fr.FR_ERR_SHAPE),
+    (dict(H=32768 + 16), fr.FR_ERR_UNSUPPORTED),
+    (dict(wmode=3), fr.FR_ERR_MODE),
+    (dict(global_scale=0.0), fr.FR_ERR_MODE),
+    (dict(global_scale=float("inf")), fr.FR_ERR_MODE),
+    (dict(global_scale=-1.0), fr.FR_ERR_MODE),
+    (dict(dtype=7), fr.FR_ERR_DTYPE),
+    (dict(T=0), fr.FR_OK),
+])
+def test_resid_rmsnorm_nvfp4_validation(kw, status):
+    args = dict(x=A, residual=B, residual_out=C, weight=D_, wmode=fr.W_NONE,
+                eps=1e-6, global_scale=1.0 / 448, out_fp4=E, out_scales=F, T=0, H=1040,
+                dtype=fr.F16)
+    args.update(kw)
+    order = ["x", "residual", "residual_out", "weight", "wmode", "eps", "global_scale",
+             "out_fp4", "out_scales", "T", "H", "dtype"]
+    assert fr.lib.fr_resid_rmsnorm_nvfp4(*[args[k] for k in order], None) == status
+
+
 @pytest.mark.parametrize("args,status", [
     ((None, 0, B, C, 10, 6144, fr.BF16), fr.FR_ERR_NULL),
     ((A, 0, B, None, 10, 6144, fr.BF16), fr.FR_ERR_NULL),
@@ -226,6 +252,7 @@ def test_resid_rmsnorm_mxfp4_validation(kw, status):
     ((A, 3, B, C, 10, 6144, fr.BF16), fr.FR_ERR_MODE),
     ((A, 0, B, C, 10, 6112, fr.BF16), fr.FR_ERR_SHAPE),
     ((A, 0, B + 2, C, 10, 6144, fr.BF16), fr.FR_ERR_ALIGN),
+    ((A, 0, B, C + 2, 10, 6144, fr.BF16), fr.FR_ERR_ALIGN),     # E8M0 codes: 4-byte stores
     ((A, 0, B, C, 10, 6144, 9), fr.FR_ERR_DTYPE),
     ((A, 0, B, C, 0, 6144, fr.BF16), fr.FR_OK),
 ])

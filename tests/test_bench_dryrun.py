@@ -113,6 +113,14 @@ def _fake_library(al, calls):
         need("mx_norm", q, T * H // 2, "out_fp4")
         need("mx_norm", s, T * H // 32, "out_scales")
 
+    def nv_norm(x, r, ro, w, wmode, eps, g, q, s, T, H, dt, stream=None):
+        calls.append("nv_norm")
+        assert g > 0
+        for p, n in ((x, "x"), (r, "residual"), (ro, "residual_out")):
+            need("nv_norm", p, T * H * 2, n)
+        need("nv_norm", q, T * H // 2, "out_fp4")
+        need("nv_norm", s, T * H // 16, "out_scales")
+
     def mx_act(gu, a, q, s, T, I, dt, stream=None):
         calls.append("mx_act")
         need("mx_act", gu, T * 2 * I * 2, "gate_up")
@@ -153,6 +161,7 @@ def _fake_library(al, calls):
                      ("fr_qkv_normrope_kvwrite", qkv), ("fr_gated_act_fp8", act),
                      ("fr_gemm_gated_act_fp8", gemm), ("fr_gemm_pack_weights", pack),
                      ("fr_resid_rmsnorm_mxfp4", mx_norm), ("fr_gated_act_mxfp4", mx_act),
+                     ("fr_resid_rmsnorm_nvfp4", nv_norm),
                      ("fr_resid_layernorm_mxfp4", ln_mx), ("fr_qk_norm_rope", qknr),
                      ("fr_decode_chain_persistent", chain)):
         setattr(fr, name, fn)
@@ -235,6 +244,6 @@ def test_bench_calls_stay_inside_their_buffers(monkeypatch):
     monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "4", "--warmup", "1",
                                       "--no-cpu-baseline", "--chain-replays", "2"])
     bench.main()
-    for op in ("resid", "ada", "qkv", "act", "gemm", "mx_norm", "mx_act", "ln_mx", "qknr",
+    for op in ("resid", "ada", "qkv", "act", "gemm", "mx_norm", "nv_norm", "mx_act", "ln_mx", "qknr",
                "chain", "copy"):
         assert op in calls, f"bench made no {op} call"
