@@ -150,14 +150,27 @@ def test_decode_chain_persistent_kernel():
         assert int(err.item()) == 0
 
 
-def test_decode_chain_persistent_small_bf16_interleaved():
-    """A smaller chain in bf16 with interleaved RoPE, 3 KV heads, 17 tokens
-    (two rows per wave for some waves) and a paged table of 4 pages."""
+SMALL_CHAINS = [
+    # (name, L, S, T, H, Hq, Hkv, D, P, pages, dtype, style, theta, mult, seed)
+    ("bf16_interleaved_T17_H512", 3, 2, 17, 512, 4, 3, 64, 8, 4, 1, 1, 5e5, 40.0, 909),
+    # rows that do not fill every lane's chunks (the guarded kernel form):
+    # 768 = 1.5 x 512 (two chunks per lane, the second partly), 256 (one
+    # chunk per lane, half the lanes idle)
+    ("f16_H768_T10", 2, 3, 10, 768, 8, 1, 256, 1024, 1, 0, 0, 1e4, 56.0, 910),
+    ("bf16_H256_T5", 2, 2, 5, 256, 2, 2, 128, 4, 3, 1, 0, 1e6, 56.0, 911),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CHAINS, ids=lambda c: c[0])
+def test_decode_chain_persistent_small(case):
+    """Smaller chains through the persistent kernel against the oracle
+    replaying the same calls: bf16 / interleaved RoPE / 3 KV heads / 17
+    tokens (two rows per wave for some waves) / a paged table, and widths
+    that do not fill whole 512-value lane rows."""
     import memory_bound_amd as fr
-    announce("decode chain persistent: bf16, interleaved, T=17")
-    rng = np.random.default_rng(909)
-    L, S, T, H, Hq, Hkv, D, P, pages = 3, 2, 17, 512, 4, 3, 64, 8, 4
-    BF = 1
+    name, L, S, T, H, Hq, Hkv, D, P, pages, BF, style, theta, mult, seed = case
+    announce(f"decode chain persistent: {name}")
+    rng = np.random.default_rng(seed)
     N = L * S
     x = workloads.to16(rng.standard_normal((L, T, H), dtype=np.float32), BF)
     gate = workloads.to16(0.1 * rng.standard_normal((N, T, H), dtype=np.float32), BF)
@@ -179,10 +192,10 @@ def test_decode_chain_persistent_small_bf16_interleaved():
     for s in range(S):
         for l in range(L):
             res[n + 1], q8[n], _ = oracle.adarms_gate_res_fp8(
-                x[l], gate[n], res[n], sc[n], sh[n], EPS, oracle.Q_STATIC, 40.0, BF)
+                x[l], gate[n], res[n], sc[n], sh[n], EPS, oracle.Q_STATIC, mult, BF)
             qo[l], err = oracle.qkv_normrope_kvwrite(
-                qkv[l], None, None, EPS, pos, 5e5, oracle.ROPE_INTERLEAVED,
-                kc[l], vc[l], table, P, Hq, Hkv, D, BF)
+                qkv[l], None, None, EPS, pos, theta, style, kc[l], vc[l], table, P, Hq,
+                Hkv, D, BF)
             assert err == 0
             n += 1
     # device
@@ -192,8 +205,8 @@ def test_decode_chain_persistent_small_bf16_interleaved():
     dqo = torch.full((L, T, Hq, D), 0x7E01, dtype=torch.int16, device="cuda")
     dkc, dvc = to_dev(kc0), to_dev(vc0)
     fr.fr_decode_chain_persistent(
-        to_dev(x), to_dev(gate), to_dev(sc), to_dev(sh), dres, dq8, EPS, 40.0,
-        to_dev(qkv), to_dev(pos), 5e5, fr.ROPE_INTERLEAVED, dqo, dkc, dvc,
+        to_dev(x), to_dev(gate), to_dev(sc), to_dev(sh), dres, dq8, EPS, mult,
+        to_dev(qkv), to_dev(pos), theta, style, dqo, dkc, dvc,
         to_dev(table), pages, P, pages, None, L, S, T, H, Hq, Hkv, D, BF)
     torch.cuda.synchronize()
     check_exact(to_host(dres, np.uint16), res, "residual chain")

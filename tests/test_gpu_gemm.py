@@ -243,6 +243,7 @@ GEMM_CASES = [
     (1000, 2048, 6144, oracle.ACT_SQRELU, 709),          # 64-row tiles (768), ragged
     (1024, 4096, 6144, oracle.ACT_SWIGLU, 710),          # 64-row tiles, K = 4096
     (96, 16384, 256, oracle.ACT_SWIGLU, 711),            # largest K
+    (100, 256, 17920, oracle.ACT_GEGLU_TANH, 712),       # 128-row tile with M < 128 (140 tiles)
 ]
 
 
