@@ -4,6 +4,10 @@ Kernel durations (per-kernel launch count, average, median, min):
     rocprofv3 --kernel-trace --stats -d <dir> -o bench -- python3 bench.py --steps 10 --no-cpu-baseline
     python3 bench_profile.py trace <dir>/bench_results.db
 
+LDS counters (one pass):
+    rocprofv3 --pmc SQ_LDS_BANK_CONFLICT ... -d <dir> -o lds --output-format csv -- python3 bench.py --pmc-pass
+    python3 bench_profile.py lds <dir>/lds_counter_collection.csv
+
 HBM byte counters of the 8192-token ops:
     rocprofv3 --pmc FETCH_SIZE -d <dir_f> -o fetch -- python3 bench.py --pmc-pass
     rocprofv3 --pmc WRITE_SIZE -d <dir_w> -o write -- python3 bench.py --pmc-pass
@@ -30,10 +34,10 @@ GIB = 1 << 30
 
 ACT_FP8 = "void fr::k_act<1, 0, 4, true, false, false>"
 KERNELS = {  # kernel name prefix -> (op, algorithmic read bytes, write bytes)
-    "void fr::k_norm<1, 2, 1, true, true, false>": (
+    "void fr::k_norm<1, 2, 1, true, true, false, false>": (
         "resid_rmsnorm_fp8 T=8192 H=4096 bf16 MUL TOKEN",
         8192 * 4096 * 4 + 4096 * 2, 8192 * 4096 * 3 + 8192 * 4),
-    "void fr::k_norm<0, 2, 3, true, false, false>": (
+    "void fr::k_norm<0, 2, 3, true, false, false, false>": (
         "adarms_gate_res_fp8 T=8192 H=1024 f16 STATIC",
         8192 * 1024 * 10, 8192 * 1024 * 3),
     "void fr::k_qkv<1, 8, true": (
@@ -42,13 +46,16 @@ KERNELS = {  # kernel name prefix -> (op, algorithmic read bytes, write bytes)
     ACT_FP8: (
         "gated_act_fp8 T=8192 I=12288 bf16 SwiGLU",
         8192 * 24576 * 2, 8192 * 12288 + 8192 * 96 * 4),
-    "void fr::k_norm<1, 2, 1, true, true, true>": (
+    "void fr::k_norm<1, 2, 1, true, true, true, false>": (
         "resid_rmsnorm_mxfp4 T=8192 H=4096 bf16 MUL",
         8192 * 4096 * 4 + 4096 * 2, 8192 * 4096 * 2 + 8192 * 2048 + 8192 * 128),
+    "void fr::k_norm<1, 2, 1, true, true, false, true>": (
+        "resid_rmsnorm_nvfp4 T=8192 H=4096 bf16 MUL",
+        8192 * 4096 * 4 + 4096 * 2, 8192 * 4096 * 2 + 8192 * 2048 + 8192 * 256),
     "void fr::k_act<1, 0, 4, true, false, true>": (
         "gated_act_mxfp4 T=8192 I=12288 bf16 SwiGLU",
         8192 * 24576 * 2, 8192 * 6144 + 8192 * 384),
-    "void fr::k_norm<1, 2, 4, true, true, true>": (
+    "void fr::k_norm<1, 2, 4, true, true, true, false>": (
         "resid_layernorm_mxfp4 T=8192 H=4096 bf16",
         8192 * 4096 * 4 + 4096 * 4, 8192 * 4096 * 2 + 8192 * 2048 + 8192 * 128),
     "void fr::k_qknr<1, 8, 4>": (
@@ -156,11 +163,53 @@ def pmc(fetch_db, write_db):
             fh.write("\n")
 
 
+LDS_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS",
+                "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES")
+
+
+def lds(csv_path):
+    """LDS counters per kernel from one rocprofv3 --pmc pass written as CSV
+    (mean over the kernel's dispatches)."""
+    import csv
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(csv_path) as fh:
+        for row in csv.DictReader(fh):
+            name = re.sub(r"^void ", "", row["Kernel_Name"]).split("(")[0]
+            acc[name][row["Counter_Name"]].append(float(row["Counter_Value"]))
+    lines = [
+        "LDS counters per kernel, rocprofv3 PMC (MI355X, gfx950)",
+        "command (one pass; the bench's PMC workload: each op a few times at its bench shape):",
+        "  rocprofv3 --pmc " + " ".join(LDS_COUNTERS) + " \\",
+        "    -d gpurun_out/pmclds -o lds --output-format csv -- python3 -u bench.py --pmc-pass",
+        "  python3 bench_profile.py lds gpurun_out/pmclds/lds_counter_collection.csv",
+        "values: mean over the kernel's dispatches; conflict% = SQ_LDS_BANK_CONFLICT / "
+        "SQ_LDS_IDX_ACTIVE; lds-issue wait% = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES",
+        "",
+        f"{'kernel':62s} {'LDS insts':>10s} {'active':>10s} {'conflict':>10s} "
+        f"{'conflict%':>9s} {'wait%':>6s}",
+    ]
+    for name, cs in sorted(acc.items()):
+        m = {k: (sum(v) / len(v) if v else 0.0) for k, v in cs.items()}
+        if not m.get("SQ_INSTS_LDS"):
+            continue
+        act = m.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        conf = m.get("SQ_LDS_BANK_CONFLICT", 0.0)
+        cyc = m.get("SQ_WAVE_CYCLES", 0.0)
+        lines.append(f"{name[:62]:62s} {m['SQ_INSTS_LDS']:10.3g} {act:10.3g} {conf:10.3g} "
+                     f"{(100 * conf / act if act else 0):8.1f}% "
+                     f"{(100 * m.get('SQ_WAIT_INST_LDS', 0.0) / cyc if cyc else 0):5.1f}%")
+    with open(os.path.join(HERE, "profiles", "lds_bank_conflicts_bench_T8192.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     os.makedirs(os.path.join(HERE, "profiles"), exist_ok=True)
     if sys.argv[1] == "trace":
         trace(sys.argv[2])
     elif sys.argv[1] == "pmc":
         pmc(sys.argv[2], sys.argv[3])
+    elif sys.argv[1] == "lds":
+        lds(sys.argv[2])
     else:
-        sys.exit("usage: bench_profile.py trace <db> | pmc <fetch_db> <write_db>")
+        sys.exit("usage: bench_profile.py trace <db> | pmc <fetch_db> <write_db> | lds <csv>")
