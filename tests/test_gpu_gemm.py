@@ -244,6 +244,9 @@ GEMM_CASES = [
     (1024, 4096, 6144, oracle.ACT_SWIGLU, 710),          # 64-row tiles, K = 4096
     (96, 16384, 256, oracle.ACT_SWIGLU, 711),            # largest K
     (100, 256, 17920, oracle.ACT_GEGLU_TANH, 712),       # 128-row tile with M < 128 (140 tiles)
+    (33, 512, 2048, oracle.ACT_SQRELU, 713),             # one row past a 32-row tile
+    (250, 1024, 1024, oracle.ACT_GEGLU_TANH, 714),       # ragged 64-row tiles
+    (129, 128, 16384, oracle.ACT_SWIGLU, 715),           # 128 output blocks, ragged
 ]
 
 
@@ -330,3 +333,30 @@ def test_gemm_determinism(fr):
         again = run_gemm(fr, inp, oracle.ACT_SWIGLU)
         assert np.array_equal(first[0], again[0])
         assert np.array_equal(first[1].view(np.uint32), again[1].view(np.uint32))
+
+
+def test_gemm_two_streams(fr):
+    """Launches on two streams that overlap give the outputs of one launch at
+    a time (the kernel keeps no state between launches)."""
+    announce("gemm two streams, overlapping launches")
+    M, K, I = 128, 1024, 4096
+    inps = [workloads.gemm_inputs(M, K, I, 720 + i) for i in range(2)]
+    refs = [run_gemm(fr, inp, oracle.ACT_SWIGLU) for inp in inps]
+    bufs = []
+    for inp in inps:
+        bufs.append({
+            "a": to_dev(inp["a"]), "a_s": to_dev(inp["a_scales"]),
+            "w": pack_dev(fr, inp["w"]), "w_s": to_dev(inp["w_scales"]),
+            "q": torch.full((M, I), 0x7F, dtype=torch.uint8, device="cuda"),
+            "sc": torch.full((M, I // 128), float("nan"), dtype=torch.float32,
+                             device="cuda")})
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(4):
+        for b, st in zip(bufs, streams):
+            fr.fr_gemm_gated_act_fp8(b["a"], b["a_s"], b["w"], b["w_s"], oracle.ACT_SWIGLU,
+                                     b["q"], b["sc"], M, K, I, stream=st)
+    torch.cuda.synchronize()
+    for b, (q_r, s_r) in zip(bufs, refs):
+        assert np.array_equal(to_host(b["q"], np.uint8), q_r)
+        assert np.array_equal(to_host(b["sc"], np.float32).view(np.uint32), s_r.view(np.uint32))
