@@ -321,12 +321,13 @@ __device__ __forceinline__ void sincos_pos(double x, float* s_out, float* c_out)
     cp = fma(cp, r2, 4.1666666666666664e-02);           // 1/4!
     cp = fma(cp, r2, -0.5);                             // 1/2!
     const double cs = fma(cp, r2, 1.0);
+    // quadrant q: (sin, cos) = (sn, cs), (cs, -sn), (-sn, -cs), (-cs, sn);
+    // selects rather than branches (q differs between lanes)
     const int q = (int)((long long)k & 3);
-    double s, c;
-    if (q == 0) { s = sn; c = cs; }
-    else if (q == 1) { s = cs; c = -sn; }
-    else if (q == 2) { s = -sn; c = -cs; }
-    else { s = -cs; c = sn; }
+    double s = (q & 1) ? cs : sn;
+    double c = (q & 1) ? sn : cs;
+    s = (q & 2) ? -s : s;
+    c = ((q + 1) & 2) ? -c : c;
     *s_out = (float)s;
     *c_out = (float)c;
 }

@@ -39,6 +39,17 @@ template <int DT, int LP, bool NT, int STYLE, bool NTS = NT>
 __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
     __shared__ float tab[4][2][128];                     // per-wave cos / sin
 
+    // Every kernel argument the kernel reads, consumed here so that they are
+    // fetched in one batch of scalar loads (one memory trip) rather than in
+    // dependent batches as each is first needed; the arguments span three
+    // scalar-cache lines, and at a handful of tokens each trip is a visible
+    // share of the kernel's time.
+    asm volatile("" ::"s"(a.qkv), "s"(a.qw), "s"(a.kw), "s"(a.pos), "s"(a.table),
+                 "s"(a.q_out), "s"(a.kc), "s"(a.vc), "s"(a.err), "s"(a.tasks), "s"(a.Hq),
+                 "s"(a.Hkv), "s"(a.D), "s"(a.groups), "s"(a.gpw), "s"(a.wpt),
+                 "s"(a.table_len), "s"(a.page_size), "s"(a.num_pages), "s"(a.eps),
+                 "s"(a.q_scale), "s"(a.l2t), "s"(a.inv_d));
+
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t task = (int64_t)blockIdx.x * 4 + wv;
@@ -69,6 +80,24 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         x0 = NT ? ld128_stream(src) : ld128(src);
         x1 = NT ? ld128_stream(src + D) : ld128(src + D);
     };
+    // Token metadata.  Small batches (latency: each wave's chain of memory
+    // trips is its time) issue it before the row as vector loads, which
+    // complete in order, so waiting for them does not wait for the row and
+    // a wait for a kernel argument does not wait for them: the position
+    // (the same word in every lane) and the first 64 page-table entries
+    // (entry i in lane i; the table holds at least one), so that for tables
+    // of up to 64 entries the slot needs no second trip once the position is
+    // known.  Large batches (bandwidth) read the position and then its page
+    // entry through the scalar cache, which adds no vector loads per wave.
+    typedef const __attribute__((address_space(4))) int32_t* cptr;
+    int posv = 0, tv = 0;
+    if constexpr (!NT) {
+        int z;                                           // 0, opaque to the compiler,
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));       // so the load stays a vector load
+        posv = a.pos[t + z];
+        tv = a.table[min(lane, a.table_len - 1)];
+    }
+
     u32x4 n0, n1;
     load_group(0, n0, n1);
     u32x4 qw0 = {0, 0, 0, 0}, qw1 = qw0, kw0 = qw0, kw1 = qw0;
@@ -77,26 +106,20 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         if (a.kw) { kw0 = ld128((const char*)a.kw + off0); kw1 = ld128((const char*)a.kw + off1); }
     }
 
-    // Token metadata (uniform across the wave), read through the scalar
-    // cache so that its dependent loads do not wait behind the row loads.
-    typedef const __attribute__((address_space(4))) int32_t* cptr;
-    const int pos = *((cptr)(uintptr_t)a.pos + t);
+    int pos;
     int64_t slot = -1;
-    if (pos >= 0) {
-        const int idx = pos / a.page_size;
-        if (idx < a.table_len) {
-            const int page = *((cptr)(uintptr_t)a.table + idx);
-            if (page >= 0 && page < a.num_pages)
-                slot = (int64_t)page * a.page_size + pos % a.page_size;
-        }
-    }
-    if (slot < 0 && g0 == 0 && lane == 0 && a.err != nullptr)
-        __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-    // cos/sin table of the token: angle i = pos * theta^(-2i/D), i < D/2.
+    auto page_slot = [&](int page) {
+        if (page >= 0 && page < a.num_pages) slot = (int64_t)page * a.page_size + pos % a.page_size;
+    };
     float* cs_tab = tab[wv][0];
     float* sn_tab = tab[wv][1];
-    {
+    if constexpr (NT) {
+        pos = *((cptr)(uintptr_t)a.pos + t);
+        if (pos >= 0) {
+            const int idx = pos / a.page_size;
+            if (idx < a.table_len) page_slot(*((cptr)(uintptr_t)a.table + idx));
+        }
+        // cos/sin table of the token: angle i = pos * theta^(-2i/D), i < D/2.
         for (int i = lane; i < (D >> 1); i += 64) {
             const double f = exp2((double)i * a.l2t);
             float sv, cv;
@@ -104,10 +127,40 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
             cs_tab[i] = cv;
             sn_tab[i] = sv;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+        // Rotation frequencies theta^(-2i/D) of this lane's angles i = lane
+        // and lane + 64 (D/2 <= 128): they do not depend on the token, so
+        // they are computed while its position is in flight; then both
+        // angles at once (two independent fp64 chains), then the stores.
+        double fq[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) fq[k] = exp2((double)(lane + 64 * k) * a.l2t);
+        asm volatile("" ::"v"(fq[0]), "v"(fq[1]));      // computed here, not sunk
+        pos = __builtin_amdgcn_readfirstlane(posv);
+        float sv[2], cv[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) sincos_pos((double)pos * fq[k], &sv[k], &cv[k]);
+        asm volatile("" ::"v"(sv[0]), "v"(sv[1]), "v"(cv[0]), "v"(cv[1]));
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int i = lane + 64 * k;
+            if (i < (D >> 1)) {
+                cs_tab[i] = cv[k];
+                sn_tab[i] = sv[k];
+            }
+        }
+        if (pos >= 0) {
+            const int idx = pos / a.page_size;
+            if (idx < a.table_len)
+                page_slot(idx < 64 ? __builtin_amdgcn_readlane(tv, idx)
+                                   : *((cptr)(uintptr_t)a.table + idx));
+        }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (slot < 0 && g0 == 0 && lane == 0 && a.err != nullptr)
+        __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // This lane's pairs: rotate-half pair e = (8j+e, D/2+8j+e) turns by
     // angle 8j+e; interleaved pair m of chunk 0 = (8j+2m, 8j+2m+1) by angle
     // 4j+m, pair m of chunk 1 by angle D/4+4j+m.
