@@ -105,6 +105,9 @@ def lib():
         L.oracle_resid_layernorm.argtypes = [
             _P, _P, _P, _P, _P, _F, _INT, _P, _INT, _F, _P, _P, _I64, _I64, _INT]
         L.oracle_resid_layernorm.restype = _INT
+        L.oracle_resid_layernorm_nvfp4.argtypes = [
+            _P, _P, _P, _P, _P, _F, _F, _P, _P, _I64, _I64, _INT]
+        L.oracle_resid_layernorm_nvfp4.restype = _INT
         L.or_layernorm.argtypes = [_P, _P, _P, _I64, _D, _P]
         L.or_layernorm.restype = None
         L.or_rope3d.argtypes = [_P, _I64, _P, _P, _D, _INT]
@@ -461,6 +464,24 @@ def resid_layernorm(x, residual, weight, bias, eps, out_kind, qmode, static_scal
         _ptr(q), qmode, static_scale, _ptr(scf), _ptr(sc8), T, H, dtype)
     assert rc == 0
     return ro, q, (sc8 if out_kind == 1 else scf)
+
+
+def resid_layernorm_nvfp4(x, residual, weight, bias, eps, global_scale, dtype):
+    """Returns (residual_out uint16 [T,H], out_fp4 uint8 [T,H/2],
+    out_scales uint8 [T,H/16] E4M3 block scale codes)."""
+    x = _c(x, np.uint16)
+    residual = _c(residual, np.uint16)
+    T, H = x.shape
+    weight = _c(weight, np.uint16)
+    bias = None if bias is None else _c(bias, np.uint16)
+    ro = np.empty_like(x)
+    q = np.empty((T, H // 2), np.uint8)
+    sc = np.empty((T, H // 16), np.uint8)
+    rc = lib().oracle_resid_layernorm_nvfp4(
+        _ptr(x), _ptr(residual), _ptr(ro), _ptr(weight), _ptr(bias), eps, global_scale,
+        _ptr(q), _ptr(sc), T, H, dtype)
+    assert rc == 0
+    return ro, q, sc
 
 
 def qk_norm_rope(qkv, norm_kind, norm_scope, q_norm_w, q_norm_b, k_norm_w,

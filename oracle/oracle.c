@@ -598,6 +598,45 @@ int oracle_resid_layernorm(const uint16_t* x, const uint16_t* residual,
     return 0;
 }
 
+/* Residual add + LayerNorm + NVFP4 [HY 06 census: the ViT add + LayerNorm
+ * producer to NVFP4 (add_layer_norm_to_nvfp4)]: the new residual and the
+ * LayerNorm output y of the op above, then or_quant_nvfp4 of each row with
+ * the caller's fp32 tensor scale.  H % 16 == 0. */
+int oracle_resid_layernorm_nvfp4(const uint16_t* x, const uint16_t* residual,
+                                 uint16_t* residual_out, const uint16_t* weight,
+                                 const uint16_t* bias, float eps, float global_scale,
+                                 uint8_t* out_fp4, uint8_t* out_scales, int64_t T,
+                                 int64_t H, int dtype)
+{
+    if (H % 16 != 0)
+        return -2;
+    double* ro = malloc(sizeof(double) * (size_t)H);
+    double* w = malloc(sizeof(double) * (size_t)H);
+    double* b = malloc(sizeof(double) * (size_t)H);
+    double* y = malloc(sizeof(double) * (size_t)H);
+    if (!ro || !w || !b || !y) {
+        free(ro); free(w); free(b); free(y);
+        return -1;
+    }
+    for (int64_t j = 0; j < H; ++j) {
+        w[j] = dec16(weight[j], dtype);
+        b[j] = bias ? dec16(bias[j], dtype) : 0.0;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t j = 0; j < H; ++j) {
+            uint16_t c = enc16(dec16(x[t * H + j], dtype) + dec16(residual[t * H + j], dtype),
+                               dtype);
+            residual_out[t * H + j] = c;
+            ro[j] = dec16(c, dtype);
+        }
+        or_layernorm(ro, w, b, H, (double)eps, y);
+        or_quant_nvfp4(y, H, (double)global_scale, out_fp4 + t * (H / 2),
+                       out_scales + t * (H / 16));
+    }
+    free(ro); free(w); free(b); free(y);
+    return 0;
+}
+
 /* Gate multiply + residual + adaptive RMSNorm + FP8 [FR section 三]:
  *   residual_out = round(residual + gate * x)
  *   y = RMSNorm(residual_out) * (1 + ada_scale) + ada_shift

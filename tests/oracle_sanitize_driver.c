@@ -66,6 +66,9 @@ static void norm_ops(int64_t T, int64_t H, int dtype)
     }
     snprintf(name, sizeof name, "resid_rmsnorm_nvfp4 T%lld H%lld", (long long)T, (long long)H);
     expect(name, oracle_resid_rmsnorm_nvfp4(x, r, ro, w, 2, 1e-6f, 0.02f, q, s8, T, H, dtype), 0);
+    snprintf(name, sizeof name, "resid_layernorm_nvfp4 T%lld H%lld", (long long)T, (long long)H);
+    expect(name, oracle_resid_layernorm_nvfp4(x, r, ro, w, b, 1e-6f, 0.02f, q, s8, T, H, dtype), 0);
+    expect(name, oracle_resid_layernorm_nvfp4(x, r, ro, w, NULL, 1e-6f, 3.0f, q, s8, T, H, dtype), 0);
     snprintf(name, sizeof name, "resid_layernorm fp8 T%lld H%lld", (long long)T, (long long)H);
     expect(name, oracle_resid_layernorm(x, r, ro, w, NULL, 1e-6f, 0, q, 1, 0.0f, fs, s8, T, H, dtype), 0);
     free(x); free(r); free(ro); free(g); free(sc); free(sh); free(w); free(b); free(q); free(s8); free(fs);

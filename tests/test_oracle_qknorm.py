@@ -152,3 +152,27 @@ def test_resid_layernorm_composes_pinned_pieces(out_kind, qmode):
             s = np.float32(max(np.abs(y).max(), np.float32(1e-10)) / 448.0)
             assert sc[t] == s
             assert np.array_equal(q[t], oracle.e4m3_encode_n(y / np.float64(s)))
+
+
+@pytest.mark.parametrize("with_bias,g", [(True, 3.7e-2), (False, 2.5e-4), (True, 400.0)])
+def test_resid_layernorm_nvfp4_composes_pinned_pieces(with_bias, g):
+    """Add + LayerNorm -> NVFP4 is the pinned NVFP4 quantiser applied to the
+    pinned LayerNorm of the same new residual as the FP8 producer; the tensor
+    scales include one that saturates block scales (2.5e-4) and one that
+    sends most blocks' scales to zero (400)."""
+    dt = oracle.BF16
+    T, H = 3, 256
+    inp = workloads.resid_rmsnorm_inputs(T, H, dt, seed=42, outliers=True)
+    rng = np.random.default_rng(43)
+    bias = workloads.to16(0.1 * rng.standard_normal(H).astype(np.float32), dt) if with_bias else None
+    ro, q, sc = oracle.resid_layernorm_nvfp4(inp["x"], inp["residual"], inp["weight"], bias,
+                                             EPS, g, dt)
+    ro8, _, _ = oracle.resid_rmsnorm_fp8(inp["x"], inp["residual"], None, oracle.W_NONE,
+                                         EPS, oracle.Q_STATIC, 1.0, dt)
+    assert np.array_equal(ro, ro8)
+    w = oracle.decode16(inp["weight"], dt)
+    b = oracle.decode16(bias, dt) if with_bias else np.zeros(H)
+    for t in range(T):
+        y = oracle.layernorm(oracle.decode16(ro[t], dt), w, b, EPS)
+        pw, sw = oracle.quant_nvfp4(y, g)
+        assert np.array_equal(q[t], pw) and np.array_equal(sc[t], sw)
