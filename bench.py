@@ -745,7 +745,8 @@ NVFP4_SCALE = 3.7e-2        # tensor dequant scale of the NVFP4 producer (amax ~
 def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
     """The FP4 producers at the bandwidth shapes (8192 tokens: RMSNorm
     H=4096 bf16 with weight -> MXFP4 and -> NVFP4, add + LayerNorm ->
-    MXFP4, SwiGLU I=12288 bf16 -> MXFP4), buffers rotated through >= 512 MB;
+    MXFP4 and -> NVFP4, SwiGLU I=12288 bf16 -> MXFP4), buffers rotated
+    through >= 512 MB;
     reps launches back to back, events at the ends."""
     T, H, I = T_BIG, 4096, 12288
     e = 2
@@ -794,11 +795,18 @@ def run_mxfp4(torch, fr, workloads, dev, stream, reps, timed=True):
         fr.fr_resid_layernorm_mxfp4(d["x"], d["residual"], d["ro"], d["weight"], bias,
                                     EPS, d["q"], d["s"], T, H, fr.BF16, stream=stream)
 
+    def ln_nv(i):
+        d = N[i % len(N)]
+        fr.fr_resid_layernorm_nvfp4(d["x"], d["residual"], d["ro"], d["weight"], bias,
+                                    EPS, NVFP4_SCALE, d["q"], d["s16"], T, H, fr.BF16,
+                                    stream=stream)
+
     out = {}
     for name, f, nb in (("resid_rmsnorm_mxfp4_T8192_H4096", norm, nb_norm),
                         ("resid_rmsnorm_nvfp4_T8192_H4096", nv, nb_nv),
                         ("gated_act_mxfp4_T8192_I12288", act, nb_act),
-                        ("resid_layernorm_mxfp4_T8192_H4096", ln, nb_ln)):
+                        ("resid_layernorm_mxfp4_T8192_H4096", ln, nb_ln),
+                        ("resid_layernorm_nvfp4_T8192_H4096", ln_nv, nb_nv + H * 2)):
         for i in range(3):
             f(i)
         torch.cuda.synchronize()

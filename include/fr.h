@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FR_ABI_VERSION 2   /* 2: fr_resid_rmsnorm_nvfp4 added */
+#define FR_ABI_VERSION 3   /* 2: fr_resid_rmsnorm_nvfp4; 3: fr_resid_layernorm_nvfp4 */
 
 typedef enum {
     FR_OK = 0,
@@ -248,8 +248,9 @@ int fr_resid_rmsnorm_nvfp4(const void* x, const void* residual,
                            void* stream);
 
 /*
- * (a-ln) residual add + LayerNorm + FP8 or MXFP4 [HY 06 census: the ViT
- *   add + LayerNorm FP4 producer; FR 二 table step 1 for the fused FP8 form]
+ * (a-ln) residual add + LayerNorm + FP8, MXFP4 or NVFP4 [HY 06 census: the
+ *   ViT add + LayerNorm FP4 producer (add_layer_norm_to_nvfp4); FR 二 table
+ *   step 1 for the fused FP8 form]
  *
  *   residual_out = round_dtype(x + residual) (bit-exact, as op (a));
  *   y = (residual_out - mean) / sqrt(var + eps) * weight + bias, mean and
@@ -259,7 +260,13 @@ int fr_resid_rmsnorm_nvfp4(const void* x, const void* residual,
  *   FR_Q_TOKEN scale); out_fp8 [T,H], out_scales [T] (token mode).
  *   _mxfp4: MXFP4 as fr_resid_rmsnorm_mxfp4; out_fp4 [T,H/2], out_scales
  *   [T,H/32]; H % 32 == 0.
- *   weight: [H] required; all tensors 16-byte aligned.
+ *   _nvfp4: NVFP4 as fr_resid_rmsnorm_nvfp4 (blocks of 16, E4M3 block
+ *   codes, caller's tensor scale global_scale > 0 and finite, FR_ERR_MODE
+ *   otherwise), taken on the fp32 y (the block code on a double-precision
+ *   amax / (6 g)); out_fp4 [T,H/2], out_scales [T,H/16] E4M3 codes (any
+ *   alignment); H % 16 == 0.
+ *   weight: [H] required; all tensors 16-byte aligned (except _nvfp4's
+ *   out_scales).
  */
 int fr_resid_layernorm_fp8(const void* x, const void* residual,
                            void* residual_out, const void* weight,
@@ -271,6 +278,11 @@ int fr_resid_layernorm_mxfp4(const void* x, const void* residual,
                              const void* bias, float eps, uint8_t* out_fp4,
                              uint8_t* out_scales, int64_t T, int64_t H,
                              int dtype, void* stream);
+int fr_resid_layernorm_nvfp4(const void* x, const void* residual,
+                             void* residual_out, const void* weight,
+                             const void* bias, float eps, float global_scale,
+                             uint8_t* out_fp4, uint8_t* out_scales, int64_t T,
+                             int64_t H, int dtype, void* stream);
 
 /*
  * (c-fp4) gated activation + MXFP4: h = act(g) * u as fr_gated_act_fp8 (fp32

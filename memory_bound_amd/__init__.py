@@ -66,6 +66,8 @@ _SIGS = {
                                _I64, _INT, _P],
     "fr_resid_layernorm_mxfp4": [_P, _P, _P, _P, _P, _F, _P, _P, _I64, _I64,
                                  _INT, _P],
+    "fr_resid_layernorm_nvfp4": [_P, _P, _P, _P, _P, _F, _F, _P, _P, _I64, _I64,
+                                 _INT, _P],
     "fr_qk_norm_rope": [_P, _INT, _INT, _P, _P, _P, _P, _F, _P, _INT, _I32,
                         _I32, _I32, _F, _INT, _F, _P, _P, _P, _I64, _I32, _I32,
                         _I32, _INT, _P],
@@ -228,6 +230,15 @@ def fr_resid_layernorm_mxfp4(x, residual, residual_out, weight, bias, eps,
     _check(lib.fr_resid_layernorm_mxfp4(
         _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(weight), _ptr(bias),
         eps, _ptr(out_fp4), _ptr(out_scales), T, H, dtype, _stream(stream)))
+
+
+def fr_resid_layernorm_nvfp4(x, residual, residual_out, weight, bias, eps,
+                             global_scale, out_fp4, out_scales, T, H, dtype,
+                             stream=None):
+    _check(lib.fr_resid_layernorm_nvfp4(
+        _ptr(x), _ptr(residual), _ptr(residual_out), _ptr(weight), _ptr(bias),
+        eps, global_scale, _ptr(out_fp4), _ptr(out_scales), T, H, dtype,
+        _stream(stream)))
 
 
 def fr_qk_norm_rope(qkv, norm_kind, norm_scope, q_norm_w, q_norm_b, k_norm_w,

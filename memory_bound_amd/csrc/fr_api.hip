@@ -311,6 +311,38 @@ FR_EXPORT int fr_resid_layernorm_mxfp4(const void* x, const void* residual,
     return launch_status(fr::launch_norm(a, dtype, fr::NORM_LAYER_MXFP4, (hipStream_t)stream));
 }
 
+FR_EXPORT int fr_resid_layernorm_nvfp4(const void* x, const void* residual,
+                                       void* residual_out, const void* weight,
+                                       const void* bias, float eps, float global_scale,
+                                       uint8_t* out_fp4, uint8_t* out_scales, int64_t T,
+                                       int64_t H, int dtype, void* stream) {
+    if (dtype != FR_F16 && dtype != FR_BF16) return FR_ERR_DTYPE;
+    if (T < 0 || H <= 0 || H % 16 != 0) return FR_ERR_SHAPE;
+    if (H > 32768 || T > 0x7fffffffLL) return FR_ERR_UNSUPPORTED;
+    if (!finite_nonneg(eps)) return FR_ERR_MODE;
+    if (!(isfinite(global_scale) && global_scale > 0.0f)) return FR_ERR_MODE;
+    if (!x || !residual || !residual_out || !weight || !out_fp4 || !out_scales) return FR_ERR_NULL;
+    if (!aligned16(x) || !aligned16(residual) || !aligned16(residual_out) ||
+        !aligned16(weight) || !aligned16(out_fp4))
+        return FR_ERR_ALIGN;
+    if (bias && !aligned16(bias)) return FR_ERR_ALIGN;
+    if (T == 0) return FR_OK;
+    fr::NormArgs a{};
+    a.x = x;
+    a.res = residual;
+    a.res_out = residual_out;
+    a.w = weight;
+    a.b = bias;
+    a.out = out_fp4;
+    a.mx_scales = out_scales;
+    a.T = T;
+    a.H = (int)H;
+    a.eps = eps;
+    a.static_scale = 1.0f;
+    a.gscale = global_scale;
+    return launch_status(fr::launch_norm(a, dtype, fr::NORM_LAYER_NVFP4, (hipStream_t)stream));
+}
+
 FR_EXPORT int fr_gated_act_mxfp4(const void* gate_up, int act, uint8_t* out_fp4,
                                  uint8_t* out_scales, int64_t T, int64_t I,
                                  int dtype, void* stream) {

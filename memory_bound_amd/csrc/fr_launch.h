@@ -147,7 +147,7 @@ struct QkNormArgs {
 hipError_t launch_qknr(const QkNormArgs& a, int dtype, hipStream_t s);
 
 enum { NORM_FP8 = 0, NORM_ADA_FP8 = 1, NORM_MXFP4 = 2, NORM_LAYER_FP8 = 3, NORM_LAYER_MXFP4 = 4,
-       NORM_NVFP4 = 5 };
+       NORM_NVFP4 = 5, NORM_LAYER_NVFP4 = 6 };
 hipError_t launch_norm(const NormArgs& a, int dtype, int kind, hipStream_t s);
 hipError_t launch_qkv(const QkvArgs& a, int dtype, hipStream_t s);
 hipError_t launch_act(const ActArgs& a, int dtype, int act, bool mx, hipStream_t s);

@@ -65,7 +65,7 @@ __device__ __forceinline__ void st_out(void* p, u32x2 v) {
 
 // NTL / NTS: non-temporal loads of the streamed inputs / stores of the
 // outputs (the norm weight is re-read by every row and stays cached).
-// MX / NV: MX FP4 or NVFP4 output instead of FP8 (plain modes; MX also
+// MX / NV: MX FP4 or NVFP4 output instead of FP8 (plain modes and
 // LayerNorm).
 template <int DT, int CPL, int MODE, bool NTL, bool NTS = NTL, bool MX = false, bool NV = false>
 __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
@@ -198,6 +198,44 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
                                        hi16<DT>(bv[k][e]));
                 if (ok[k]) amax = fmaxf(amax, fmaxf(fabsf(y[k][2 * e]), fabsf(y[k][2 * e + 1])));
             }
+        }
+        if constexpr (NV) {
+            // NVFP4: a block of 16 values is a lane pair.  The block scale
+            // code is E4M3(amax / (6 g)) of the fp32 y: amax / (6 g) in
+            // double, rounded to odd into fp32 so the saturating conversion
+            // rounds the double value; the elements are E2M1(y / S) with
+            // S = e4m3(code) * g, y * (1 / S) formed in double and rounded
+            // to odd into fp32 before the E2M1 conversion.
+            uint8_t* orow4 = a.out + t * (int64_t)(a.H >> 1);
+            uint8_t* srow = a.mx_scales + t * (int64_t)(a.H >> 4);
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                float m = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(y[k][e]));
+                m = group_reduce<2>(m, OpMaxMag());      // the block's other lane
+                const double sd = (double)m * a.inv6g;
+                const float sh = (float)sd;
+                const float sf = round_odd(sh, (float)(sd - (double)sh));
+                const int code = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(sf), 0.0f, 0, false) & 0xFF;
+                const double S = (double)__builtin_amdgcn_cvt_f32_fp8(code, 0) * (double)a.gscale;
+                const double Kd = S > 0.0 ? rcp_d(S) : 0.0;
+                float q[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double v = (double)y[k][e] * Kd;
+                    const float vh = (float)v;
+                    q[e] = round_odd(vh, (float)(v - (double)vh));
+                }
+                const u32 pk = pack_e2m1x8(q, 1.0f);
+                if (ok[k] && row_ok) {
+                    const int c = k * stride + ww * 64 + lane;
+                    u32* dst = (u32*)(orow4 + c * 4);
+                    if constexpr (NTS) __builtin_nontemporal_store(pk, dst); else *dst = pk;
+                    if ((lane & 1) == 0) srow[c >> 1] = (uint8_t)code;
+                }
+            }
+            return;
         }
         if constexpr (MX) {
             uint8_t* orow4 = a.out + t * (int64_t)(a.H >> 1);
@@ -471,6 +509,7 @@ static hipError_t launch_norm_dt(const NormArgs& a, int mode, bool mx, bool nv, 
         switch (mode) {
         case M_NONE: return launch_norm_mode<DT, M_NONE, NT, false, true>(a, cpl, s);
         case M_MUL: return launch_norm_mode<DT, M_MUL, NT, false, true>(a, cpl, s);
+        case M_LAYER: return launch_norm_mode<DT, M_LAYER, NT, false, true>(a, cpl, s);
         default: return launch_norm_mode<DT, M_ONE_PLUS, NT, false, true>(a, cpl, s);
         }
     }
@@ -524,9 +563,9 @@ static NormShape pick_norm_shape(int64_t T, int H, bool adaptive) {
 hipError_t launch_norm(const NormArgs& in, int dtype, int kind, hipStream_t s) {
     NormArgs a = in;
     const bool adaptive = kind == NORM_ADA_FP8;
-    const bool layer = kind == NORM_LAYER_FP8 || kind == NORM_LAYER_MXFP4;
+    const bool layer = kind == NORM_LAYER_FP8 || kind == NORM_LAYER_MXFP4 || kind == NORM_LAYER_NVFP4;
     const bool mx = kind == NORM_MXFP4 || kind == NORM_LAYER_MXFP4;
-    const bool nv = kind == NORM_NVFP4;
+    const bool nv = kind == NORM_NVFP4 || kind == NORM_LAYER_NVFP4;
     const NormShape sh = pick_norm_shape(a.T, a.H, adaptive);
     a.inv_h = 1.0 / (double)a.H;
     if (nv) a.inv6g = 1.0 / (6.0 * (double)a.gscale);

@@ -31,7 +31,8 @@ def test_header_declares_the_four_ops_and_helpers():
         "fr_gemm_pack_weights", "fr_resid_rmsnorm_mxfp4", "fr_gated_act_mxfp4",
         "fr_resid_rmsnorm_nvfp4",
         "fr_decode_chain_persistent", "fr_qk_norm_rope", "fr_resid_layernorm_fp8",
-        "fr_resid_layernorm_mxfp4", "fr_status_string", "fr_abi_version"])
+        "fr_resid_layernorm_mxfp4", "fr_resid_layernorm_nvfp4", "fr_status_string",
+        "fr_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert fr.abi_version() == 2
+    assert fr.abi_version() == 3
     for s in range(8):
         assert fr.status_string(s).startswith("FR_")
     assert fr.status_string(99) == "unknown fr_status"
@@ -352,3 +353,24 @@ def test_resid_layernorm_fp8_validation(args, status):
 ])
 def test_resid_layernorm_mxfp4_validation(args, status):
     assert fr.lib.fr_resid_layernorm_mxfp4(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, C, None, None, 1e-6, 0.02, E, F, 10, 1040, fr.F16), fr.FR_ERR_NULL),
+    ((A, B, C, D_, None, 1e-6, 0.02, E, None, 10, 1040, fr.F16), fr.FR_ERR_NULL),
+    ((A, B, C, D_, None, 1e-6, 0.02, E, F, 10, 1032, fr.F16), fr.FR_ERR_SHAPE),
+    ((A, B, C, D_, None, 1e-6, 0.02, E, F, 10, 32784, fr.F16), fr.FR_ERR_UNSUPPORTED),
+    ((A, B, C, D_, None, 1e-6, 0.0, E, F, 10, 1040, fr.F16), fr.FR_ERR_MODE),
+    ((A, B, C, D_, None, 1e-6, float("nan"), E, F, 10, 1040, fr.F16), fr.FR_ERR_MODE),
+    ((A, B, C, D_, None, -1.0, 0.02, E, F, 10, 1040, fr.F16), fr.FR_ERR_MODE),
+    ((A, B, C, D_, None, 1e-6, 0.02, E + 8, F, 10, 1040, fr.F16), fr.FR_ERR_ALIGN),
+    ((A, B, C, D_, G + 4, 1e-6, 0.02, E, F, 10, 1040, fr.F16), fr.FR_ERR_ALIGN),
+    ((A, B, C, D_, None, 1e-6, 0.02, E, F + 1, 0, 1040, fr.F16), fr.FR_OK),
+    ((A, B, C, D_, None, 1e-6, 0.02, E, F, 10, 1040, 9), fr.FR_ERR_DTYPE),
+    ((A, B, C, D_, G, 1e-6, 0.02, E, F, 0, 1040, fr.BF16), fr.FR_OK),
+])
+def test_resid_layernorm_nvfp4_validation(args, status):
+    """Add + LayerNorm -> NVFP4: H % 16, the tensor scale, alignment (the
+    block-scale codes may sit at any byte), dtype; no launch happens (T = 0
+    or an error)."""
+    assert fr.lib.fr_resid_layernorm_nvfp4(*args, None) == status

@@ -134,6 +134,15 @@ def _fake_library(al, calls):
         need("ln_mx", q, T * H // 2, "out_fp4")
         need("ln_mx", s, T * H // 32, "out_scales")
 
+    def ln_nv(x, r, ro, w, b, eps, g, q, s, T, H, dt, stream=None):
+        calls.append("ln_nv")
+        assert g > 0
+        for p, n in ((x, "x"), (r, "residual"), (ro, "residual_out")):
+            need("ln_nv", p, T * H * 2, n)
+        need("ln_nv", w, H * 2, "weight")
+        need("ln_nv", q, T * H // 2, "out_fp4")
+        need("ln_nv", s, T * H // 16, "out_scales")
+
     def qknr(qkv_, kind, full, qw, qb, kw, kb, eps, pos, rd, sec, theta, style, qs, qo, ko,
              vo, T, Hq, Hkv, D, dt, stream=None):
         calls.append("qknr")
@@ -162,7 +171,8 @@ def _fake_library(al, calls):
                      ("fr_gemm_gated_act_fp8", gemm), ("fr_gemm_pack_weights", pack),
                      ("fr_resid_rmsnorm_mxfp4", mx_norm), ("fr_gated_act_mxfp4", mx_act),
                      ("fr_resid_rmsnorm_nvfp4", nv_norm),
-                     ("fr_resid_layernorm_mxfp4", ln_mx), ("fr_qk_norm_rope", qknr),
+                     ("fr_resid_layernorm_mxfp4", ln_mx), ("fr_resid_layernorm_nvfp4", ln_nv),
+                     ("fr_qk_norm_rope", qknr),
                      ("fr_decode_chain_persistent", chain)):
         setattr(fr, name, fn)
     hg = types.ModuleType("memory_bound_amd.hipgraph")
@@ -244,6 +254,6 @@ def test_bench_calls_stay_inside_their_buffers(monkeypatch):
     monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "4", "--warmup", "1",
                                       "--no-cpu-baseline", "--chain-replays", "2"])
     bench.main()
-    for op in ("resid", "ada", "qkv", "act", "gemm", "mx_norm", "nv_norm", "mx_act", "ln_mx", "qknr",
+    for op in ("resid", "ada", "qkv", "act", "gemm", "mx_norm", "nv_norm", "mx_act", "ln_mx", "ln_nv", "qknr",
                "chain", "copy"):
         assert op in calls, f"bench made no {op} call"

@@ -148,6 +148,11 @@ QKV_CASES = [
     ("d256_norm", 7, 2, 2, 256, BF16, True, 1e6, 1, 16, 1, False, None, 405),
     ("far_positions", 16, 4, 1, 128, BF16, True, 1e6, 0, 4096, 64, True,
      np.arange(200000, 200016), 406),
+    # a small batch whose page-table indices reach past the 64 entries the
+    # kernel holds in registers (indices 0..255 of a 256-entry table)
+    ("long_page_table", 12, 4, 2, 64, BF16, True, 1e4, 0, 16, 256, True,
+     np.array([3, 63 * 16 + 15, 64 * 16, 64 * 16 + 1, 100 * 16 + 7, 127 * 16 + 15,
+               128 * 16, 200 * 16 + 3, 255 * 16 + 15, 17, 1000, 4000]), 409),
     ("bench_8192", 8192, 32, 8, 128, BF16, True, 1e6, 0, 16, 512, True, None, 103),
 ]
 
