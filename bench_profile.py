@@ -58,6 +58,9 @@ KERNELS = {  # kernel name prefix -> (op, algorithmic read bytes, write bytes)
     "void fr::k_norm<1, 2, 4, true, true, true, false>": (
         "resid_layernorm_mxfp4 T=8192 H=4096 bf16",
         8192 * 4096 * 4 + 4096 * 4, 8192 * 4096 * 2 + 8192 * 2048 + 8192 * 128),
+    "void fr::k_norm<1, 2, 4, true, true, false, true>": (
+        "resid_layernorm_nvfp4 T=8192 H=4096 bf16",
+        8192 * 4096 * 4 + 4096 * 4, 8192 * 4096 * 2 + 8192 * 2048 + 8192 * 256),
     "void fr::k_qknr<1, 8, 4>": (
         "qk_norm_rope T=8192 40/40x128 bf16 RMS full 3D (Wan)",
         8192 * 120 * 128 * 2 + 8192 * 12 + 2 * 5120 * 2 * 2, 8192 * 120 * 128 * 2),
