@@ -203,9 +203,11 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
             // NVFP4: a block of 16 values is a lane pair.  The block scale
             // code is E4M3(amax / (6 g)) of the fp32 y: amax / (6 g) in
             // double, rounded to odd into fp32 so the saturating conversion
-            // rounds the double value; the elements are E2M1(y / S) with
-            // S = e4m3(code) * g, y * (1 / S) formed in double and rounded
-            // to odd into fp32 before the E2M1 conversion.
+            // rounds the double value; the elements are E2M1(y * K) with
+            // K = 1 / S in fp32, S = e4m3(code) * g (y itself is fp32, so a
+            // wider product would not bring the codes closer to the exact
+            // ones; K is clamped to the fp32 range for tiny scales, where
+            // every nonzero y saturates either way).
             uint8_t* orow4 = a.out + t * (int64_t)(a.H >> 1);
             uint8_t* srow = a.mx_scales + t * (int64_t)(a.H >> 4);
 #pragma unroll
@@ -219,15 +221,8 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
                 const float sf = round_odd(sh, (float)(sd - (double)sh));
                 const int code = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(sf), 0.0f, 0, false) & 0xFF;
                 const double S = (double)__builtin_amdgcn_cvt_f32_fp8(code, 0) * (double)a.gscale;
-                const double Kd = S > 0.0 ? rcp_d(S) : 0.0;
-                float q[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const double v = (double)y[k][e] * Kd;
-                    const float vh = (float)v;
-                    q[e] = round_odd(vh, (float)(v - (double)vh));
-                }
-                const u32 pk = pack_e2m1x8(q, 1.0f);
+                const float K = S > 0.0 ? (float)fmin(rcp_d(S), 3.4028234663852886e38) : 0.0f;
+                const u32 pk = pack_e2m1x8(y[k], K);
                 if (ok[k] && row_ok) {
                     const int c = k * stride + ww * 64 + lane;
                     u32* dst = (u32*)(orow4 + c * 4);
