@@ -7,13 +7,15 @@
 // of gate + residual + AdaRMSNorm + FP8, with QKV post-processing per layer,
 // and launch count dominates).
 //
-// Every output location of the chain belongs to one wave for the whole
-// chain: wave t (t < T) runs op (a') on token row t for every op n = s L + l
-// in order; each further wave owns a fixed set of (token, head) units and
-// runs op (b) on them for every op in order.  The only value one op hands
-// to the next is the residual row, and it stays in the registers of its row
-// wave (it is still stored, as each op's output).  So program order within
-// each wave is all the ordering the chain needs: no barrier and no grid-wide
+// Every output location of the chain belongs to one wave (or, for rows wider
+// than 512 values, one pair of waves) for the whole chain: row t's waves run
+// op (a') on token row t for every op n = s L + l in order; each further
+// wave owns a fixed set of (token, head) units and runs op (b) on them for
+// every op in order.  The only value one op hands to the next is the
+// residual row, and it stays in the registers of its row waves (it is still
+// stored, as each op's output).  So program order within each wave is all
+// the ordering the chain needs, apart from the sum of squares that a row's
+// two waves exchange per op inside their own workgroup: no grid-wide
 // synchronisation (nothing can deadlock).  What remains serial is the
 // residual hand-off of each row; every input load is independent of it, so
 // each wave keeps the inputs of its next few ops in flight in a register
@@ -33,25 +35,42 @@ namespace fr {
 // FULL: every lane's CPL chunks are inside the row (H = 512 CPL), so the
 // stores need no guard and consecutive ops form one basic block the
 // compiler can interleave.
-template <int DT, int CPL, int LP, int PA, int PB, bool FULL>
+//
+// NWR = 2: a row is split over two waves (wave half h takes the 64-chunk
+// blocks 2k + h), which halves each wave's work per op, the serial part of
+// the chain.  The two waves add their fp64 partial sums through LDS behind a
+// barrier, so row waves get workgroups of their own (two rows each; for odd
+// T the spare row's waves run the same ops on a duplicate row and store
+// nothing, so every barrier is reached by all four waves), and the unit
+// waves follow in further workgroups.
+template <int DT, int CPL, int LP, int PA, int PB, bool FULL, int NWR>
 __global__ __launch_bounds__(256) void k_chain(ChainArgs a) {
+    __shared__ double red[2][4];                         // [op parity][wave]
     const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);  // global wave
+    const int wave = threadIdx.x >> 6;
     const int T = a.T, H = a.H, D = a.D;
     const int N = a.layers * a.steps;
     const int64_t rowb = (int64_t)H * 2;                 // bytes per 16-bit row
     const int64_t step_rows = (int64_t)T * rowb;         // one op's [T,H] in bytes
+    const int row_wgs = NWR == 1 ? 0 : (T + 1) / 2;     // workgroups of row waves
+    const bool row_wave = NWR == 1 ? blockIdx.x * 4 + wave < T : (int)blockIdx.x < row_wgs;
+    // unit-wave index (op (b) waves are numbered after the row waves)
+    const int ug = NWR == 1 ? blockIdx.x * 4 + wave - T : ((int)blockIdx.x - row_wgs) * 4 + wave;
 
-    if (gw < T) {
+    if (row_wave) {
         // ---------------- row wave: op (a') for row t, every op ----------
-        const int t = gw;
+        const int t_raw = NWR == 1 ? blockIdx.x * 4 + wave : blockIdx.x * 2 + (wave >> 1);
+        const bool row_ok = t_raw < T;
+        const int t = row_ok ? t_raw : T - 1;            // in-bounds duplicate
+        const int half = NWR == 1 ? 0 : (wave & 1);
         const int C = H >> 3;
         int cc[CPL];
         bool ok[CPL];
 #pragma unroll
         for (int k = 0; k < CPL; ++k) {
-            ok[k] = FULL || k * 64 + lane < C;
-            cc[k] = min(k * 64 + lane, C - 1) * 16;      // byte offset of the chunk
+            const int c = (k * NWR + half) * 64 + lane;
+            ok[k] = FULL || c < C;
+            cc[k] = min(c, C - 1) * 16;                  // byte offset of the chunk
         }
         u32x4 rres[CPL];
 #pragma unroll
@@ -90,10 +109,17 @@ __global__ __launch_bounds__(256) void k_chain(ChainArgs a) {
                 }
                 if (ok[k]) {
                     ss += c0 + c1;
-                    st128((char*)a.res + nr + step_rows + cc[k], rres[k]);
+                    if (row_ok) st128((char*)a.res + nr + step_rows + cc[k], rres[k]);
                 }
             }
             ss = wave_sum_d(ss);
+            if constexpr (NWR == 2) {
+                // the other half of the row; both waves add the two partials
+                // in the same order, so they get the same rstd
+                if (lane == 0) red[n & 1][wave] = ss;
+                __syncthreads();
+                ss = red[n & 1][wave & ~1] + red[n & 1][wave | 1];
+            }
             const float rstd = (float)rsqrt_d(ss * (1.0 / (double)H) + (double)a.eps);
             const float mult = a.static_scale;
             uint8_t* orow = a.out + (int64_t)n * T * H + (int64_t)t * H;
@@ -107,7 +133,7 @@ __global__ __launch_bounds__(256) void k_chain(ChainArgs a) {
                     y[2 * e] = fmaf(n0, 1.0f + lo16<DT>(sv[d][k][e]), lo16<DT>(hv[d][k][e]));
                     y[2 * e + 1] = fmaf(n1, 1.0f + hi16<DT>(sv[d][k][e]), hi16<DT>(hv[d][k][e]));
                 }
-                if (ok[k]) {
+                if (ok[k] && row_ok) {
                     u32x2 q;
                     q.x = pack_e4m3x4(y[0] * mult, y[1] * mult, y[2] * mult, y[3] * mult);
                     q.y = pack_e4m3x4(y[4] * mult, y[5] * mult, y[6] * mult, y[7] * mult);
@@ -134,7 +160,7 @@ __global__ __launch_bounds__(256) void k_chain(ChainArgs a) {
     // ---------------- unit wave: op (b) for HPW fixed (token, head) units ---
     constexpr int HPW = 64 / LP;
     const int NH = a.Hq + 2 * a.Hkv;
-    const int u = (gw - T) * HPW + lane / LP;
+    const int u = ug * HPW + lane / LP;
     const int j = lane & (LP - 1);
     if (u >= T * NH || j >= (D >> 4)) return;            // lanes without work
     const int t = u / NH, head = u - t * NH;
@@ -252,39 +278,44 @@ __global__ __launch_bounds__(256) void k_chain(ChainArgs a) {
 constexpr int kChainPA = 4;      // op (a') inputs in flight per row wave
 constexpr int kChainPB = 8;      // op (b) inputs in flight per unit wave
 
-template <int DT, int CPL, bool FULL>
+template <int DT, int CPL, bool FULL, int NWR>
 static hipError_t launch_chain_cpl(const ChainArgs& a, int lp, hipStream_t s) {
     const void* fn;
     switch (lp) {
-    case 1: fn = (const void*)k_chain<DT, CPL, 1, kChainPA, kChainPB, FULL>; break;
-    case 2: fn = (const void*)k_chain<DT, CPL, 2, kChainPA, kChainPB, FULL>; break;
-    case 4: fn = (const void*)k_chain<DT, CPL, 4, kChainPA, kChainPB, FULL>; break;
-    case 8: fn = (const void*)k_chain<DT, CPL, 8, kChainPA, kChainPB, FULL>; break;
-    default: fn = (const void*)k_chain<DT, CPL, 16, kChainPA, kChainPB, FULL>; break;
+    case 1: fn = (const void*)k_chain<DT, CPL, 1, kChainPA, kChainPB, FULL, NWR>; break;
+    case 2: fn = (const void*)k_chain<DT, CPL, 2, kChainPA, kChainPB, FULL, NWR>; break;
+    case 4: fn = (const void*)k_chain<DT, CPL, 4, kChainPA, kChainPB, FULL, NWR>; break;
+    case 8: fn = (const void*)k_chain<DT, CPL, 8, kChainPA, kChainPB, FULL, NWR>; break;
+    default: fn = (const void*)k_chain<DT, CPL, 16, kChainPA, kChainPB, FULL, NWR>; break;
     }
     const int units = a.T * (a.Hq + 2 * a.Hkv);
     const int hpw = 64 / lp;
-    const int waves = a.T + (units + hpw - 1) / hpw;     // row waves, then unit waves
+    const int unit_waves = (units + hpw - 1) / hpw;
+    // row waves, then unit waves; with two waves per row the rows fill
+    // workgroups of their own (two rows each)
+    const int blocks = NWR == 1 ? (a.T + unit_waves + 3) / 4 : (a.T + 1) / 2 + (unit_waves + 3) / 4;
     ChainArgs copy = a;
     void* args[] = {&copy};
-    return hipLaunchKernel(fn, dim3((unsigned)((waves + 3) / 4)), dim3(256), args, 0, s);
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, s);
 }
 
+// Rows of up to 512 values take one wave each (one 16-byte chunk per lane);
+// wider rows (up to 1024) are split over two waves, which halves the serial
+// work per op on the row's path.
 template <int DT>
-static hipError_t launch_chain_dt(const ChainArgs& a, int cpl, int lp, hipStream_t s) {
-    const bool full = a.H == 512 * cpl;
-    if (cpl == 1)
-        return full ? launch_chain_cpl<DT, 1, true>(a, lp, s) : launch_chain_cpl<DT, 1, false>(a, lp, s);
-    return full ? launch_chain_cpl<DT, 2, true>(a, lp, s) : launch_chain_cpl<DT, 2, false>(a, lp, s);
+static hipError_t launch_chain_dt(const ChainArgs& a, int lp, hipStream_t s) {
+    if (a.H <= 512)
+        return a.H == 512 ? launch_chain_cpl<DT, 1, true, 1>(a, lp, s)
+                          : launch_chain_cpl<DT, 1, false, 1>(a, lp, s);
+    return a.H == 1024 ? launch_chain_cpl<DT, 1, true, 2>(a, lp, s)
+                       : launch_chain_cpl<DT, 1, false, 2>(a, lp, s);
 }
 
 hipError_t launch_chain(const ChainArgs& a, int dtype, hipStream_t s) {
-    const int C = a.H / 8;
-    const int cpl = C <= 64 ? 1 : 2;                     // H <= kChainMaxH
-    int lp = 1;
+    int lp = 1;                                          // H <= kChainMaxH = 1024
     while (lp < a.D / 16) lp *= 2;
-    return dtype == DT_BF16 ? launch_chain_dt<DT_BF16>(a, cpl, lp, s)
-                            : launch_chain_dt<DT_F16>(a, cpl, lp, s);
+    return dtype == DT_BF16 ? launch_chain_dt<DT_BF16>(a, lp, s)
+                            : launch_chain_dt<DT_F16>(a, lp, s);
 }
 
 }  // namespace fr

@@ -100,7 +100,7 @@ struct PackArgs {
 // The decoder-step chain (op a' then op b per layer and flow step) in one
 // persistent launch: one wave per token row, further waves per head units.
 constexpr int kChainMaxT = 64;
-constexpr int kChainMaxH = 2 * 64 * 8;          // two 8-value chunks per lane
+constexpr int kChainMaxH = 2 * 64 * 8;          // one 8-value chunk per lane of two waves
 struct ChainArgs {
     const void* x;          // [layers, T, H]
     const void* gate;       // [N, T, H]  (N = layers * steps)
