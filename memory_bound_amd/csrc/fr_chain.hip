@@ -36,57 +36,78 @@ namespace fr {
 // stores need no guard and consecutive ops form one basic block the
 // compiler can interleave.
 //
-// NWR = 2: a row is split over two waves (wave half h takes the 64-chunk
-// blocks 2k + h), which halves each wave's work per op, the serial part of
-// the chain.  The two waves add their fp64 partial sums through LDS behind a
-// barrier, so row waves get workgroups of their own (two rows each; for odd
-// T the spare row's waves run the same ops on a duplicate row and store
+// NWR > 1: a row is split over NWR waves (wave part p takes the 64-chunk
+// blocks NWR k + p), which divides each wave's work per op, the serial part
+// of the chain.  The row's waves add their fp64 partial sums through LDS
+// behind a barrier, so row waves get workgroups of their own (4 / NWR rows
+// each; spare rows' waves run the same ops on a duplicate row and store
 // nothing, so every barrier is reached by all four waves), and the unit
 // waves follow in further workgroups.
-template <int DT, int CPL, int LP, int PA, int PB, bool FULL, int NWR>
+// CW: 32-bit words per lane chunk (4: 8 values, 16-byte loads; 2: 4 values,
+// 8-byte loads, for rows split over four waves).
+template <int W> struct ChunkT;
+template <> struct ChunkT<4> {
+    typedef u32x4 type;
+    static __device__ __forceinline__ type ld(const void* p) { return ld128(p); }
+    static __device__ __forceinline__ void st(void* p, type v) { st128(p, v); }
+};
+template <> struct ChunkT<2> {
+    typedef u32x2 type;
+    static __device__ __forceinline__ type ld(const void* p) {
+        return *reinterpret_cast<const u32x2*>(p);
+    }
+    static __device__ __forceinline__ void st(void* p, type v) { st64(p, v); }
+};
+
+template <int DT, int CPL, int LP, int PA, int PB, bool FULL, int NWR, int CW = 4>
 __global__ __launch_bounds__(256) void k_chain(ChainArgs a) {
-    __shared__ double red[2][4];                         // [op parity][wave]
+    constexpr int WGW = 4;                               // waves per workgroup
+    typedef ChunkT<CW> Ch;
+    typedef typename Ch::type chunk;
+    constexpr int RPW = WGW / NWR;                       // rows per row workgroup
+    __shared__ double red[2][WGW];                       // [op parity][wave]
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int T = a.T, H = a.H, D = a.D;
     const int N = a.layers * a.steps;
     const int64_t rowb = (int64_t)H * 2;                 // bytes per 16-bit row
     const int64_t step_rows = (int64_t)T * rowb;         // one op's [T,H] in bytes
-    const int row_wgs = NWR == 1 ? 0 : (T + 1) / 2;     // workgroups of row waves
-    const bool row_wave = NWR == 1 ? blockIdx.x * 4 + wave < T : (int)blockIdx.x < row_wgs;
+    const int row_wgs = NWR == 1 ? 0 : (T + RPW - 1) / RPW;   // workgroups of row waves
+    const bool row_wave = NWR == 1 ? blockIdx.x * WGW + wave < T : (int)blockIdx.x < row_wgs;
     // unit-wave index (op (b) waves are numbered after the row waves)
-    const int ug = NWR == 1 ? blockIdx.x * 4 + wave - T : ((int)blockIdx.x - row_wgs) * 4 + wave;
+    const int ug = NWR == 1 ? blockIdx.x * WGW + wave - T
+                            : ((int)blockIdx.x - row_wgs) * WGW + wave;
 
     if (row_wave) {
         // ---------------- row wave: op (a') for row t, every op ----------
-        const int t_raw = NWR == 1 ? blockIdx.x * 4 + wave : blockIdx.x * 2 + (wave >> 1);
+        const int t_raw = NWR == 1 ? blockIdx.x * WGW + wave : blockIdx.x * RPW + wave / NWR;
         const bool row_ok = t_raw < T;
         const int t = row_ok ? t_raw : T - 1;            // in-bounds duplicate
-        const int half = NWR == 1 ? 0 : (wave & 1);
-        const int C = H >> 3;
+        const int part = NWR == 1 ? 0 : wave % NWR;      // this wave's share of the row
+        const int C = H / (2 * CW);                      // chunks per row
         int cc[CPL];
         bool ok[CPL];
 #pragma unroll
         for (int k = 0; k < CPL; ++k) {
-            const int c = (k * NWR + half) * 64 + lane;
+            const int c = (k * NWR + part) * 64 + lane;
             ok[k] = FULL || c < C;
-            cc[k] = min(c, C - 1) * 16;                  // byte offset of the chunk
+            cc[k] = min(c, C - 1) * (4 * CW);            // byte offset of the chunk
         }
-        u32x4 rres[CPL];
+        chunk rres[CPL];
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) rres[k] = ld128((const char*)a.res + t * rowb + cc[k]);
+        for (int k = 0; k < CPL; ++k) rres[k] = Ch::ld((const char*)a.res + t * rowb + cc[k]);
 
-        u32x4 xv[PA][CPL], gv[PA][CPL], sv[PA][CPL], hv[PA][CPL];
+        chunk xv[PA][CPL], gv[PA][CPL], sv[PA][CPL], hv[PA][CPL];
         auto fetch = [&](int d, int n) {
             const int l = n % a.layers;
             const char* xr = (const char*)a.x + l * step_rows + t * rowb;
             const int64_t nr = (int64_t)n * step_rows + t * rowb;
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
-                xv[d][k] = ld128(xr + cc[k]);
-                gv[d][k] = ld128((const char*)a.gate + nr + cc[k]);
-                sv[d][k] = ld128((const char*)a.ada_scale + nr + cc[k]);
-                hv[d][k] = ld128((const char*)a.ada_shift + nr + cc[k]);
+                xv[d][k] = Ch::ld(xr + cc[k]);
+                gv[d][k] = Ch::ld((const char*)a.gate + nr + cc[k]);
+                sv[d][k] = Ch::ld((const char*)a.ada_scale + nr + cc[k]);
+                hv[d][k] = Ch::ld((const char*)a.ada_shift + nr + cc[k]);
             }
         };
         auto op = [&](int d, int n) {
@@ -96,7 +117,7 @@ __global__ __launch_bounds__(256) void k_chain(ChainArgs a) {
             for (int k = 0; k < CPL; ++k) {
                 double c0 = 0.0, c1 = 0.0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < CW; ++e) {
                     const float h0 = add_round_odd(lo16<DT>(rres[k][e]),
                                                    lo16<DT>(gv[d][k][e]) * lo16<DT>(xv[d][k][e]));
                     const float h1 = add_round_odd(hi16<DT>(rres[k][e]),
@@ -109,35 +130,43 @@ __global__ __launch_bounds__(256) void k_chain(ChainArgs a) {
                 }
                 if (ok[k]) {
                     ss += c0 + c1;
-                    if (row_ok) st128((char*)a.res + nr + step_rows + cc[k], rres[k]);
+                    if (row_ok) Ch::st((char*)a.res + nr + step_rows + cc[k], rres[k]);
                 }
             }
             ss = wave_sum_d(ss);
-            if constexpr (NWR == 2) {
-                // the other half of the row; both waves add the two partials
-                // in the same order, so they get the same rstd
+            if constexpr (NWR > 1) {
+                // the rest of the row; every wave of the row adds the
+                // partials in the same order, so all get the same rstd
                 if (lane == 0) red[n & 1][wave] = ss;
                 __syncthreads();
-                ss = red[n & 1][wave & ~1] + red[n & 1][wave | 1];
+                const int base = wave & ~(NWR - 1);
+                ss = red[n & 1][base];
+#pragma unroll
+                for (int w = 1; w < NWR; ++w) ss += red[n & 1][base + w];
             }
             const float rstd = (float)rsqrt_d(ss * (1.0 / (double)H) + (double)a.eps);
             const float mult = a.static_scale;
             uint8_t* orow = a.out + (int64_t)n * T * H + (int64_t)t * H;
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
-                float y[8];
+                float y[2 * CW];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < CW; ++e) {
                     const float n0 = lo16<DT>(rres[k][e]) * rstd;
                     const float n1 = hi16<DT>(rres[k][e]) * rstd;
                     y[2 * e] = fmaf(n0, 1.0f + lo16<DT>(sv[d][k][e]), lo16<DT>(hv[d][k][e]));
                     y[2 * e + 1] = fmaf(n1, 1.0f + hi16<DT>(sv[d][k][e]), hi16<DT>(hv[d][k][e]));
                 }
                 if (ok[k] && row_ok) {
-                    u32x2 q;
-                    q.x = pack_e4m3x4(y[0] * mult, y[1] * mult, y[2] * mult, y[3] * mult);
-                    q.y = pack_e4m3x4(y[4] * mult, y[5] * mult, y[6] * mult, y[7] * mult);
-                    st64(orow + cc[k] / 2, q);
+                    if constexpr (CW == 4) {
+                        u32x2 q;
+                        q.x = pack_e4m3x4(y[0] * mult, y[1] * mult, y[2] * mult, y[3] * mult);
+                        q.y = pack_e4m3x4(y[4] * mult, y[5] * mult, y[6] * mult, y[7] * mult);
+                        st64(orow + cc[k] / 2, q);
+                    } else {
+                        *reinterpret_cast<u32*>(orow + cc[k] / 2) =
+                            pack_e4m3x4(y[0] * mult, y[1] * mult, y[2] * mult, y[3] * mult);
+                    }
                 }
             }
         };
@@ -278,37 +307,43 @@ __global__ __launch_bounds__(256) void k_chain(ChainArgs a) {
 constexpr int kChainPA = 4;      // op (a') inputs in flight per row wave
 constexpr int kChainPB = 8;      // op (b) inputs in flight per unit wave
 
-template <int DT, int CPL, bool FULL, int NWR>
+template <int DT, int CPL, bool FULL, int NWR, int CW>
 static hipError_t launch_chain_cpl(const ChainArgs& a, int lp, hipStream_t s) {
     const void* fn;
     switch (lp) {
-    case 1: fn = (const void*)k_chain<DT, CPL, 1, kChainPA, kChainPB, FULL, NWR>; break;
-    case 2: fn = (const void*)k_chain<DT, CPL, 2, kChainPA, kChainPB, FULL, NWR>; break;
-    case 4: fn = (const void*)k_chain<DT, CPL, 4, kChainPA, kChainPB, FULL, NWR>; break;
-    case 8: fn = (const void*)k_chain<DT, CPL, 8, kChainPA, kChainPB, FULL, NWR>; break;
-    default: fn = (const void*)k_chain<DT, CPL, 16, kChainPA, kChainPB, FULL, NWR>; break;
+    case 1: fn = (const void*)k_chain<DT, CPL, 1, kChainPA, kChainPB, FULL, NWR, CW>; break;
+    case 2: fn = (const void*)k_chain<DT, CPL, 2, kChainPA, kChainPB, FULL, NWR, CW>; break;
+    case 4: fn = (const void*)k_chain<DT, CPL, 4, kChainPA, kChainPB, FULL, NWR, CW>; break;
+    case 8: fn = (const void*)k_chain<DT, CPL, 8, kChainPA, kChainPB, FULL, NWR, CW>; break;
+    default: fn = (const void*)k_chain<DT, CPL, 16, kChainPA, kChainPB, FULL, NWR, CW>; break;
     }
     const int units = a.T * (a.Hq + 2 * a.Hkv);
     const int hpw = 64 / lp;
     const int unit_waves = (units + hpw - 1) / hpw;
-    // row waves, then unit waves; with two waves per row the rows fill
-    // workgroups of their own (two rows each)
-    const int blocks = NWR == 1 ? (a.T + unit_waves + 3) / 4 : (a.T + 1) / 2 + (unit_waves + 3) / 4;
+    // row waves, then unit waves; with several waves per row the rows fill
+    // workgroups of their own (4 / NWR rows each)
+    constexpr int RPW = 4 / NWR;
+    const int blocks = NWR == 1 ? (a.T + unit_waves + 3) / 4
+                                : (a.T + RPW - 1) / RPW + (unit_waves + 3) / 4;
     ChainArgs copy = a;
     void* args[] = {&copy};
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, s);
 }
 
 // Rows of up to 512 values take one wave each (one 16-byte chunk per lane);
-// wider rows (up to 1024) are split over two waves, which halves the serial
-// work per op on the row's path.
+// wider rows (up to 1024) are split over the four waves of a workgroup (one
+// 8-byte chunk per lane each), which quarters the serial work per op on the
+// row's path.  Measured at 10 tokens, H = 1024 / 768, the 360-op chain:
+// one wave per row 173 / 193 us, two 130 / 133 us, four 97 / 99 us, eight
+// (512-thread workgroups, 4-byte chunks) 98 / 99 us: past four waves the
+// reduction, barrier and the fp64 rsqrt chain of each op set its time.
 template <int DT>
 static hipError_t launch_chain_dt(const ChainArgs& a, int lp, hipStream_t s) {
     if (a.H <= 512)
-        return a.H == 512 ? launch_chain_cpl<DT, 1, true, 1>(a, lp, s)
-                          : launch_chain_cpl<DT, 1, false, 1>(a, lp, s);
-    return a.H == 1024 ? launch_chain_cpl<DT, 1, true, 2>(a, lp, s)
-                       : launch_chain_cpl<DT, 1, false, 2>(a, lp, s);
+        return a.H == 512 ? launch_chain_cpl<DT, 1, true, 1, 4>(a, lp, s)
+                          : launch_chain_cpl<DT, 1, false, 1, 4>(a, lp, s);
+    return a.H == 1024 ? launch_chain_cpl<DT, 1, true, 4, 2>(a, lp, s)
+                       : launch_chain_cpl<DT, 1, false, 4, 2>(a, lp, s);
 }
 
 hipError_t launch_chain(const ChainArgs& a, int dtype, hipStream_t s) {

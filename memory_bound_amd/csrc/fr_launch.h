@@ -98,9 +98,10 @@ struct PackArgs {
 };
 
 // The decoder-step chain (op a' then op b per layer and flow step) in one
-// persistent launch: one wave per token row, further waves per head units.
+// persistent launch: one wave (or four, for rows over 512 values) per token
+// row, further waves per head units.
 constexpr int kChainMaxT = 64;
-constexpr int kChainMaxH = 2 * 64 * 8;          // one 8-value chunk per lane of two waves
+constexpr int kChainMaxH = 4 * 64 * 4;          // one 4-value chunk per lane of four waves
 struct ChainArgs {
     const void* x;          // [layers, T, H]
     const void* gate;       // [N, T, H]  (N = layers * steps)
