@@ -37,6 +37,10 @@ RMS_CASES = [
     (2049, 1040, F16, oracle.W_NONE, oracle.Q_TOKEN, 0.0, False, 206),
     (8192, 4096, BF16, oracle.W_MUL, oracle.Q_TOKEN, 0.0, True, 105),     # full bandwidth config
     (8192, 4096, BF16, oracle.W_NONE, oracle.Q_TOKEN, 0.0, True, 105),
+    # bandwidth path with rows over several waves, each workgroup taking rows in
+    # turn: (1 + w) weights with static scale, three waves per row
+    (2304, 2048, F16, oracle.W_ONE_PLUS, oracle.Q_STATIC, 56.0, False, 210),
+    (4100, 3072, BF16, oracle.W_ONE_PLUS, oracle.Q_TOKEN, 0.0, True, 211),
     (16, 256, F16, oracle.W_NONE, oracle.Q_STATIC, 1000.0, False, 207),   # saturating multiplier
     (16, 256, F16, oracle.W_NONE, oracle.Q_STATIC, 2.0 ** -8, False, 208),  # subnormal codes
 ]
@@ -57,14 +61,16 @@ def test_resid_rmsnorm(fr, case):
         check_scales(sc_g, sc_o, "out_scales")
 
 
-def test_resid_rmsnorm_in_place(fr):
-    announce("resid_rmsnorm in place T=64 H=2048")
-    inp = workloads.resid_rmsnorm_inputs(64, 2048, F16, 209)
+@pytest.mark.parametrize("T,H,dt", [(64, 2048, F16), (2100, 4096, BF16)],
+                         ids=["T64_H2048", "T2100_H4096_bandwidth"])
+def test_resid_rmsnorm_in_place(fr, T, H, dt):
+    announce(f"resid_rmsnorm in place T={T} H={H}")
+    inp = workloads.resid_rmsnorm_inputs(T, H, dt, 209)
     ro_g, q_g, sc_g = run_resid_rmsnorm(fr, inp, oracle.W_MUL, EPS,
-                                        oracle.Q_TOKEN, 0.0, F16, inplace=True)
+                                        oracle.Q_TOKEN, 0.0, dt, inplace=True)
     ro_o, q_o, sc_o = oracle.resid_rmsnorm_fp8(
         inp["x"], inp["residual"], inp["weight"], oracle.W_MUL, EPS,
-        oracle.Q_TOKEN, 0.0, F16)
+        oracle.Q_TOKEN, 0.0, dt)
     check_exact(ro_g, ro_o, "residual_out (in place)")
     check_fp8(q_g, q_o, "out_fp8")
     check_scales(sc_g, sc_o, "out_scales")
