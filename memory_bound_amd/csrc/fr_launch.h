@@ -47,11 +47,9 @@ struct QkvArgs {
     void* vc;
     int32_t* err;
     int64_t T;
-    int64_t tasks;          // T * wpt wavefronts
+    int64_t tasks;          // T * groups wavefronts
     int Hq, Hkv, D;
-    int groups;             // head groups (64/LP heads each) per token
-    int gpw;                // head groups per wavefront
-    int wpt;                // wavefronts per token
+    int groups;             // head groups (64/LP heads each) per token, one wave each
     int table_len, page_size, num_pages;
     int style;
     float eps;

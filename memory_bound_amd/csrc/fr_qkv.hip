@@ -7,20 +7,21 @@
 // in one lane so no cross-lane shuffle is needed) and the "Falcon-Perception
 // inference engine" article (paged KV cache written by the decode step).
 //
-// Mapping: a wave64 handles one token and `gpw` groups of 64/LP heads; LP
-// lanes (a power of two >= D/16) serve one head.  Lane j of a head holds the
+// Mapping: a wave64 handles one group of 64/LP heads of one token; LP lanes
+// (a power of two >= D/16) serve one head.  Lane j of a head holds the
 // 16-byte chunk j of the first half of the head and chunk j of the second
 // half, so each rotate-half pair (i, i+D/2) -- and each interleaved pair
-// (2i, 2i+1) -- sits in one lane's registers.  Each group's loads are issued
-// while the previous group is processed.  The wave index is uniform
+// (2i, 2i+1) -- sits in one lane's registers.  The wave index is uniform
 // (readfirstlane), so the token's position and page-table entry are scalar
 // loads (through the scalar cache, after the first row loads, so their
 // dependent chain does not queue behind them), and the row arithmetic runs
 // on the scalar unit.  The per-head sum of squares is a DPP reduction over
 // the LP lanes, and rstd the hardware reciprocal square root.  The D/2
 // rotation angles of the token are shared by every head: the wave computes
-// each of them once (one or two per lane) into a per-wave LDS table, then
-// every lane reads the cos/sin of its own pairs.  Angles are formed in fp64:
+// each of them once (one or two per lane) into a per-wave LDS table, and
+// every lane reads the cos/sin of its own pairs from it where they are used
+// (held in registers they would cost a wave slot per SIMD).  Each lane loads
+// only its own head's norm weight (Q or K).  Angles are formed in fp64:
 // theta^(-2i/D) = 2^(i * step) with step = -2 log2(theta) / D computed on
 // the host, times the position, reduced modulo pi/2 by a two-constant
 // Cody-Waite step with fma; sine and cosine come from Taylor polynomials on
@@ -30,8 +31,6 @@
 #include "fr_launch.h"
 
 namespace fr {
-
-constexpr int kQkvMaxGroups = 8;   // head groups one wave may take
 
 // NT: non-temporal loads of the packed rows and stores of Q, K and V (used
 // in the bandwidth regime, where nothing is re-read soon).
@@ -46,7 +45,7 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
     // share of the kernel's time.
     asm volatile("" ::"s"(a.qkv), "s"(a.qw), "s"(a.kw), "s"(a.pos), "s"(a.table),
                  "s"(a.q_out), "s"(a.kc), "s"(a.vc), "s"(a.err), "s"(a.tasks), "s"(a.Hq),
-                 "s"(a.Hkv), "s"(a.D), "s"(a.groups), "s"(a.gpw), "s"(a.wpt),
+                 "s"(a.Hkv), "s"(a.D), "s"(a.groups),
                  "s"(a.table_len), "s"(a.page_size), "s"(a.num_pages), "s"(a.eps),
                  "s"(a.q_scale), "s"(a.l2t), "s"(a.inv_d));
 
@@ -54,9 +53,8 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t task = (int64_t)blockIdx.x * 4 + wv;
     if (task >= a.tasks) return;                         // whole wave exits
-    const int64_t t = task / a.wpt;                      // token
-    const int g0 = (int)(task - t * a.wpt) * a.gpw;      // first head group
-    const int ng = min(a.gpw, a.groups - g0);            // groups of this wave
+    const int64_t t = task / a.groups;                   // token
+    const int g0 = (int)(task - t * a.groups);           // this wave's head group
 
     constexpr int HPW = 64 / LP;
     const int NH = a.Hq + 2 * a.Hkv;
@@ -65,21 +63,15 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
     const int j = lane & (LP - 1);
     const int hl = lane / LP;                            // head within a group
 
-    // Head group g of this wave: its chunks are loaded one group ahead of
-    // the group being processed.  Every lane loads (lanes past the row's
-    // heads or past D/16 re-read a valid chunk and store nothing): a load
-    // that some waves skip makes the compiler wait for every outstanding
-    // load, the prefetch included, before each group.
+    // This lane's head and chunks.  Every lane loads (lanes past the row's
+    // heads or past D/16 re-read a valid chunk and store nothing), so the
+    // compiler's waits cover exactly the loads in use.
     const char* rowp = (const char*)a.qkv + t * (int64_t)NH * D * 2;
     const int off0 = j * 16;                 // bytes of chunk j, first half
     const int off1 = D + j * 16;             // bytes of chunk j, second half
     const int jc = min(j, L - 1);
-    auto load_group = [&](int g, u32x4& x0, u32x4& x1) {          // g < ng
-        const int head = min((g0 + g) * HPW + hl, NH - 1);
-        const char* src = rowp + (int64_t)head * D * 2 + jc * 16;
-        x0 = NT ? ld128_stream(src) : ld128(src);
-        x1 = NT ? ld128_stream(src + D) : ld128(src + D);
-    };
+    const int head = g0 * HPW + hl;
+    const int head_c = min(head, NH - 1);
     // Token metadata.  Small batches (latency: each wave's chain of memory
     // trips is its time) issue it before the row as vector loads, which
     // complete in order, so waiting for them does not wait for the row and
@@ -98,12 +90,18 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
         tv = a.table[min(lane, a.table_len - 1)];
     }
 
-    u32x4 n0, n1;
-    load_group(0, n0, n1);
-    u32x4 qw0 = {0, 0, 0, 0}, qw1 = qw0, kw0 = qw0, kw1 = qw0;
-    if (j < L) {
-        if (a.qw) { qw0 = ld128((const char*)a.qw + off0); qw1 = ld128((const char*)a.qw + off1); }
-        if (a.kw) { kw0 = ld128((const char*)a.kw + off0); kw1 = ld128((const char*)a.kw + off1); }
+    u32x4 c0, c1;
+    {
+        const char* src = rowp + (int64_t)head_c * D * 2 + jc * 16;
+        c0 = NT ? ld128_stream(src) : ld128(src);
+        c1 = NT ? ld128_stream(src + D) : ld128(src + D);
+    }
+    u32x4 w0, w1;                                        // the head's norm weight
+    {
+        const char* wp = head_c < a.Hq ? (const char*)a.qw : (const char*)a.kw;
+        if (wp == nullptr) wp = rowp;                    // unused (no norm)
+        w0 = ld128(wp + jc * 16);
+        w1 = ld128(wp + D + jc * 16);
     }
 
     int pos;
@@ -161,128 +159,110 @@ __global__ __launch_bounds__(256) void k_qkv(QkvArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (slot < 0 && g0 == 0 && lane == 0 && a.err != nullptr)
         __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // This lane's pairs: rotate-half pair e = (8j+e, D/2+8j+e) turns by
-    // angle 8j+e; interleaved pair m of chunk 0 = (8j+2m, 8j+2m+1) by angle
-    // 4j+m, pair m of chunk 1 by angle D/4+4j+m.
+    const bool active = (j < L) && (head < NH);
+    const bool is_q = head < a.Hq;
+    const bool is_v = head >= a.Hq + a.Hkv;
+
+    if (is_v) {
+        if (active && slot >= 0) {
+            char* dst = (char*)a.vc + (slot * a.Hkv + (head - a.Hq - a.Hkv)) * (int64_t)D * 2;
+            if constexpr (NTS) {
+                st128_stream(dst + off0, c0);
+                st128_stream(dst + off1, c1);
+            } else {
+                st128(dst + off0, c0);
+                st128(dst + off1, c1);
+            }
+        }
+    }
+
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = lo16<DT>(c0[e]);
+        v[2 * e + 1] = hi16<DT>(c0[e]);
+        v[8 + 2 * e] = lo16<DT>(c1[e]);
+        v[8 + 2 * e + 1] = hi16<DT>(c1[e]);
+    }
+
+    // Per-head RMSNorm over D (every lane takes part in the reduction;
+    // lanes without data contribute zero).
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss = fmaf(v[e], v[e], ss);
+    if (j >= L) ss = 0.0f;                           // padding lanes hold a re-read chunk
+    ss = group_reduce<LP>(ss, OpSum());
+    const bool has_norm = !is_v && (is_q ? a.qw : a.kw) != nullptr;
+    if (has_norm) {
+        const float rstd = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_d, a.eps));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = v[2 * e] * rstd * lo16<DT>(w0[e]);
+            v[2 * e + 1] = v[2 * e + 1] * rstd * hi16<DT>(w0[e]);
+            v[8 + 2 * e] = v[8 + 2 * e] * rstd * lo16<DT>(w1[e]);
+            v[8 + 2 * e + 1] = v[8 + 2 * e + 1] * rstd * hi16<DT>(w1[e]);
+        }
+    }
+    if (!active || is_v) return;
+    // this lane's pairs: rotate-half pair e = (8j+e, D/2+8j+e) turns by
+    // angle 8j+e; interleaved pair m of chunk 0 = (8j+2m, 8j+2m+1) by
+    // angle 4j+m, pair m of chunk 1 by angle D/4+4j+m
     float cs[8], sn[8];
-    if (j < L) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int i = STYLE == 0 ? 8 * j + e
+                                   : (e < 4 ? 4 * j + e : (D >> 2) + 4 * j + (e - 4));
+        cs[e] = cs_tab[i];
+        sn[e] = sn_tab[i];
+    }
+
+    if constexpr (STYLE == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int i = STYLE == 0 ? 8 * j + e
-                                       : (e < 4 ? 4 * j + e : (D >> 2) + 4 * j + (e - 4));
-            cs[e] = cs_tab[i];
-            sn[e] = sn_tab[i];
+            const float x0 = v[e], x1 = v[8 + e];
+            v[e] = fmaf(x0, cs[e], -x1 * sn[e]);
+            v[8 + e] = fmaf(x1, cs[e], x0 * sn[e]);
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cs[e] = sn[e] = 0.0f;
+        for (int m = 0; m < 4; ++m) {
+            float x0 = v[2 * m], x1 = v[2 * m + 1];
+            v[2 * m] = fmaf(x0, cs[m], -x1 * sn[m]);
+            v[2 * m + 1] = fmaf(x1, cs[m], x0 * sn[m]);
+            x0 = v[8 + 2 * m];
+            x1 = v[8 + 2 * m + 1];
+            v[8 + 2 * m] = fmaf(x0, cs[4 + m], -x1 * sn[4 + m]);
+            v[8 + 2 * m + 1] = fmaf(x1, cs[4 + m], x0 * sn[4 + m]);
+        }
     }
 
-    auto process = [&](int g, const u32x4 c0, const u32x4 c1) {
-        const int head = (g0 + g) * HPW + hl;
-        const bool active = (j < L) && (head < NH);
-        const bool is_q = head < a.Hq;
-        const bool is_v = head >= a.Hq + a.Hkv;
-
-        if (is_v) {
-            if (active && slot >= 0) {
-                char* dst = (char*)a.vc + (slot * a.Hkv + (head - a.Hq - a.Hkv)) * (int64_t)D * 2;
-                if constexpr (NTS) {
-                    st128_stream(dst + off0, c0);
-                    st128_stream(dst + off1, c1);
-                } else {
-                    st128(dst + off0, c0);
-                    st128(dst + off1, c1);
-                }
-            }
-        }
-
-        float v[16];
+    // attention's Q pre-scale (exact for K: a multiply by 1)
+    if (a.q_scale != 1.0f) {                         // uniform
+        const float qs = is_q ? a.q_scale : 1.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[2 * e] = lo16<DT>(c0[e]);
-            v[2 * e + 1] = hi16<DT>(c0[e]);
-            v[8 + 2 * e] = lo16<DT>(c1[e]);
-            v[8 + 2 * e + 1] = hi16<DT>(c1[e]);
-        }
-
-        // Per-head RMSNorm over D (every lane takes part in the reduction;
-        // lanes without data contribute zero).
-        float ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ss = fmaf(v[e], v[e], ss);
-        if (j >= L) ss = 0.0f;                           // padding lanes hold a re-read chunk
-        ss = group_reduce<LP>(ss, OpSum());
-        const bool has_norm = !is_v && (is_q ? a.qw : a.kw) != nullptr;
-        if (has_norm) {
-            const u32x4 w0 = is_q ? qw0 : kw0, w1 = is_q ? qw1 : kw1;
-            const float rstd = __builtin_amdgcn_rsqf(fmaf(ss, a.inv_d, a.eps));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[2 * e] = v[2 * e] * rstd * lo16<DT>(w0[e]);
-                v[2 * e + 1] = v[2 * e + 1] * rstd * hi16<DT>(w0[e]);
-                v[8 + 2 * e] = v[8 + 2 * e] * rstd * lo16<DT>(w1[e]);
-                v[8 + 2 * e + 1] = v[8 + 2 * e + 1] * rstd * hi16<DT>(w1[e]);
-            }
-        }
-        if (!active || is_v) return;
-
-        if constexpr (STYLE == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x0 = v[e], x1 = v[8 + e];
-                v[e] = fmaf(x0, cs[e], -x1 * sn[e]);
-                v[8 + e] = fmaf(x1, cs[e], x0 * sn[e]);
-            }
-        } else {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                float x0 = v[2 * m], x1 = v[2 * m + 1];
-                v[2 * m] = fmaf(x0, cs[m], -x1 * sn[m]);
-                v[2 * m + 1] = fmaf(x1, cs[m], x0 * sn[m]);
-                x0 = v[8 + 2 * m];
-                x1 = v[8 + 2 * m + 1];
-                v[8 + 2 * m] = fmaf(x0, cs[4 + m], -x1 * sn[4 + m]);
-                v[8 + 2 * m + 1] = fmaf(x1, cs[4 + m], x0 * sn[4 + m]);
-            }
-        }
-
-        // attention's Q pre-scale (exact for K: a multiply by 1)
-        if (a.q_scale != 1.0f) {                         // uniform
-            const float qs = is_q ? a.q_scale : 1.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) v[e] *= qs;
-        }
-
-        u32x4 o0, o1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            o0[e] = pack16<DT>(v[2 * e], v[2 * e + 1]);
-            o1[e] = pack16<DT>(v[8 + 2 * e], v[8 + 2 * e + 1]);
-        }
-        char* dst;
-        if (is_q) {
-            dst = (char*)a.q_out + ((t * a.Hq + head) * (int64_t)D) * 2;
-        } else {
-            if (slot < 0) return;
-            dst = (char*)a.kc + (slot * a.Hkv + (head - a.Hq)) * (int64_t)D * 2;
-        }
-        if constexpr (NTS) {
-            st128_stream(dst + off0, o0);
-            st128_stream(dst + off1, o1);
-        } else {
-            st128(dst + off0, o0);
-            st128(dst + off1, o1);
-        }
-    };
-
-#pragma unroll 1
-    for (int g = 0; g + 1 < ng; ++g) {                   // uniform trip count
-        const u32x4 c0 = n0, c1 = n1;
-        load_group(g + 1, n0, n1);
-        process(g, c0, c1);
+        for (int e = 0; e < 16; ++e) v[e] *= qs;
     }
-    process(ng - 1, n0, n1);
+
+    u32x4 o0, o1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o0[e] = pack16<DT>(v[2 * e], v[2 * e + 1]);
+        o1[e] = pack16<DT>(v[8 + 2 * e], v[8 + 2 * e + 1]);
+    }
+    char* dst;
+    if (is_q) {
+        dst = (char*)a.q_out + ((t * a.Hq + head) * (int64_t)D) * 2;
+    } else {
+        if (slot < 0) return;
+        dst = (char*)a.kc + (slot * a.Hkv + (head - a.Hq)) * (int64_t)D * 2;
+    }
+    if constexpr (NTS) {
+        st128_stream(dst + off0, o0);
+        st128_stream(dst + off1, o1);
+    } else {
+        st128(dst + off0, o0);
+        st128(dst + off1, o1);
+    }
 }
 
 template <int DT, bool NT, int STYLE>
@@ -305,15 +285,15 @@ static hipError_t launch_qkv_dt(const QkvArgs& a, int lp, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, s);
 }
 
-// Head groups per wave.  In the bandwidth regime (T >= 2048) a token's groups
-// are split over two waves, so each wave's angles serve several groups and
-// consecutive groups' loads overlap, with non-temporal streaming; measured
-// on MI355X at T = 8192 (32/8 heads x 128, 6 groups): 3 groups per wave
-// 68-69% of 8 TB/s, 2 per wave 66%, 1 or 6 per wave 60%; cacheable stores
-// 63%.  A kernel with this op's loads and stores and no arithmetic reaches
-// 72.5% at 8192 tokens and 67% at 4096 (the same bytes as one plain copy
-// stream: 77% and 71%).  Small batches give each group its own wave,
-// trading repeated angle work for parallelism, and keep outputs cacheable.
+// One head group per wave at every batch size.  In the bandwidth regime
+// (T >= 2048) loads and stores are non-temporal.  Measured on MI355X at
+// T = 8192, 32/8 heads x 128 bf16 (6 groups), same-box A/B, outputs
+// identical: a token's groups split over 2 waves (a prefetch loop over 3
+// groups each, 78 registers) 36.7 us; over 3 waves 34.5 us; one group per
+// wave with the same registers 34.4 us; as here (the norm weight of the
+// lane's own head only, cos/sin read from LDS where used: 68 registers, 7
+// waves per SIMD instead of 6) 33.8 us.  At 4096 tokens 20.0 -> 18.3 us;
+// 64/8 heads at 8192 tokens 60.0 -> 53.7 us.
 hipError_t launch_qkv(const QkvArgs& in, int dtype, hipStream_t s) {
     QkvArgs a = in;
     a.l2t = -2.0 * log2((double)a.theta) / (double)a.D;   // exponent step per pair
@@ -325,14 +305,7 @@ hipError_t launch_qkv(const QkvArgs& in, int dtype, hipStream_t s) {
     const int NH = a.Hq + 2 * a.Hkv;
     const bool big = a.T >= 2048;
     a.groups = (NH + hpw - 1) / hpw;
-    if (big) {
-        a.gpw = (a.groups + 1) / 2;
-        if (a.gpw > kQkvMaxGroups) a.gpw = kQkvMaxGroups;
-    } else {
-        a.gpw = 1;
-    }
-    a.wpt = (a.groups + a.gpw - 1) / a.gpw;
-    a.tasks = a.T * a.wpt;
+    a.tasks = a.T * a.groups;
     if (dtype == DT_BF16)
         return big ? launch_qkv_dt<DT_BF16, true>(a, lp, s) : launch_qkv_dt<DT_BF16, false>(a, lp, s);
     return big ? launch_qkv_dt<DT_F16, true>(a, lp, s) : launch_qkv_dt<DT_F16, false>(a, lp, s);

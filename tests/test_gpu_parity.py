@@ -160,6 +160,9 @@ QKV_CASES = [
      np.array([3, 63 * 16 + 15, 64 * 16, 64 * 16 + 1, 100 * 16 + 7, 127 * 16 + 15,
                128 * 16, 200 * 16 + 3, 255 * 16 + 15, 17, 1000, 4000]), 409),
     ("bench_8192", 8192, 32, 8, 128, BF16, True, 1e6, 0, 16, 512, True, None, 103),
+    # bandwidth regime, 80 heads = 10 groups of 8: the token's last wave
+    # takes fewer groups than the others
+    ("wide_heads_2048", 2048, 64, 8, 128, BF16, True, 1e6, 0, 16, 128, True, None, 410),
 ]
 
 
