@@ -137,6 +137,7 @@ struct QkNormArgs {
     int Hq, Hkv, D;
     int norm_kind;          // 0 none, 1 RMS, 2 Layer
     int full;               // norm over the full Q (K) width
+    int split;              // workgroups per token (each one pass of heads), or 1
     int rope3;              // 3D RoPE
     int sec[3];             // 3D RoPE pairs per axis
     int style;

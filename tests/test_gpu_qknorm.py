@@ -31,6 +31,9 @@ CASES = [
     ("d16_rms_full", 9, 3, 3, 16, BF16, 1, True, False, None, 1, 1e4, 1.0, 607),
     ("wan_bench_8192", 8192, 40, 40, 128, BF16, 1, True, True, (22, 21, 21), 1, 1e4, 1.0, 608),
     ("chameleon_bench_8192", 8192, 32, 32, 128, BF16, 2, False, False, None, 0, 1e4, 1.0, 609),
+    # per-head norm over four full passes of heads (one workgroup per pass),
+    # 3D RoPE, interleaved pairs
+    ("rms_head_3d_four_passes", 50, 64, 32, 128, BF16, 1, False, True, (22, 21, 21), 1, 1e4, 0.5, 614),
 ]
 
 
