@@ -153,11 +153,17 @@ def test_decode_chain_persistent_kernel():
 SMALL_CHAINS = [
     # (name, L, S, T, H, Hq, Hkv, D, P, pages, dtype, style, theta, mult, seed)
     ("bf16_interleaved_T17_H512", 3, 2, 17, 512, 4, 3, 64, 8, 4, 1, 1, 5e5, 40.0, 909),
-    # rows that do not fill every lane's chunks (the guarded kernel form):
-    # 768 = 1.5 x 512 (two chunks per lane, the second partly), 256 (one
-    # chunk per lane, half the lanes idle)
+    # rows that do not fill every lane's chunks (the guarded kernel form).
+    # Rows over 512 values are split over four waves of 4-value chunks: 768
+    # (the fourth wave idle), 528 (the third wave 4 chunks, the fourth idle),
+    # 1008 (the fourth wave 60 of 64 lanes); 256 is one wave of 8-value
+    # chunks with half the lanes idle
     ("f16_H768_T10", 2, 3, 10, 768, 8, 1, 256, 1024, 1, 0, 0, 1e4, 56.0, 910),
     ("bf16_H256_T5", 2, 2, 5, 256, 2, 2, 128, 4, 3, 1, 0, 1e6, 56.0, 911),
+    ("f16_H528_T3", 2, 2, 3, 528, 2, 1, 64, 16, 1, 0, 1, 1e4, 56.0, 912),
+    ("f16_H1008_T1", 1, 3, 1, 1008, 1, 1, 256, 1024, 1, 0, 0, 1e4, 56.0, 914),
+    # the most tokens a chain takes (64), full 1024-value rows
+    ("bf16_H1024_T64", 2, 2, 64, 1024, 8, 2, 128, 16, 8, 1, 0, 1e6, 40.0, 913),
 ]
 
 
