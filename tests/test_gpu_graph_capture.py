@@ -146,11 +146,45 @@ def case_qk_norm_rope(fr):
     return call, [q, k, v]
 
 
+def case_pack_weights(fr):
+    N, K = 512, 1024
+    w = to_dev(np.random.default_rng(811).integers(0, 256, (N, K), dtype=np.uint8))
+    wp = _empty((N * K,), torch.uint8)
+    torch.cuda.synchronize()
+    def call(st):
+        fr.fr_gemm_pack_weights(w, wp, N, K, stream=st)
+    return call, [wp]
+
+
+def case_chain_persistent(fr):
+    L, S, T, H, Hq, Hkv, D, P, pages = 2, 2, 10, 1024, 8, 1, 256, 1024, 1
+    N = L * S
+    rng = np.random.default_rng(812)
+    f16 = lambda *shape, sd=1.0: to_dev(workloads.to16(
+        sd * rng.standard_normal(shape, dtype=np.float32), fr.F16))
+    x, gate, sc, sh = f16(L, T, H), f16(N, T, H, sd=0.1), f16(N, T, H, sd=0.1), f16(N, T, H, sd=0.1)
+    qkv = f16(L, T, (Hq + 2 * Hkv) * D)
+    res = _empty((N + 1, T, H), torch.int16)
+    res[0] = f16(T, H)
+    q8, qo = _empty((N, T, H), torch.uint8), _empty((L, T, Hq, D), torch.int16)
+    kc = torch.full((L, pages, P, Hkv, D), workloads.SENTINEL, dtype=torch.int16, device="cuda")
+    vc = kc.clone()
+    pos = to_dev(np.arange(790, 800, dtype=np.int32))
+    table = to_dev(np.zeros(1, np.int32))
+    torch.cuda.synchronize()                            # the fills ran on torch's stream
+    def call(st):
+        fr.fr_decode_chain_persistent(x, gate, sc, sh, res, q8, EPS, 56.0, qkv, pos, 1e4,
+                                      fr.ROPE_HALF, qo, kc, vc, table, pages, P, pages, None,
+                                      L, S, T, H, Hq, Hkv, D, fr.F16, stream=st)
+    return call, [res[1:], q8, qo], [kc, vc]          # res[0] is the chain's input
+
+
 CASES = [("resid_rmsnorm_fp8", case_resid_rmsnorm_fp8, 1), ("adarms", case_adarms, 1),
          ("qkv", case_qkv, 1), ("gated_act_fp8", case_gated_act_fp8, 1),
          ("gemm_gated_act_fp8", case_gemm, 1), ("fp4_norm_producers", case_fp4_norms, 3),
          ("layernorm_fp8_mxfp4", case_layernorm, 2), ("gated_act_mxfp4", case_gated_act_mxfp4, 1),
-         ("qk_norm_rope", case_qk_norm_rope, 1)]
+         ("qk_norm_rope", case_qk_norm_rope, 1), ("gemm_pack_weights", case_pack_weights, 1),
+         ("decode_chain_persistent", case_chain_persistent, 1)]
 
 
 def _bits(t):
