@@ -213,6 +213,30 @@ def test_qkv_q_prescale(fr, qs):
     check_exact(vc_g, vc_o, "v_cache")
 
 
+def test_qkv_bandwidth_k_norm_only_and_out_of_range(fr):
+    """Bandwidth regime (T >= 2048): K norm only (each lane loads its own
+    head's weight; Q heads take none), a head group that mixes K and V
+    heads (16/4 x 128: group 2 = K heads 0..3 and V heads 0..3), and two
+    tokens whose positions map to no slot (their K/V writes are skipped and
+    the error bit set)."""
+    T, Hq, Hkv, D, P, pages = 2048, 16, 4, 128, 16, 128
+    announce("qkv bandwidth regime, k_norm only, out-of-range positions")
+    pos = np.arange(T, dtype=np.int32)
+    pos[5], pos[1000] = -1, P * pages                      # no slot
+    inp = workloads.qkv_inputs(T, Hq, Hkv, D, BF16, 412, page_size=P,
+                               num_pages=pages, positions=pos)
+    inp["q_norm_w"] = None
+    q_g, kc_g, vc_g, err_g = run_qkv(fr, inp, EPS, 1e6, 0, Hq, Hkv, D, P, BF16)
+    kc_o, vc_o = inp["k_cache"].copy(), inp["v_cache"].copy()
+    q_o, err_o = oracle.qkv_normrope_kvwrite(
+        inp["qkv"], None, inp["k_norm_w"], EPS, pos, 1e6, 0, kc_o, vc_o,
+        inp["page_table"], P, Hq, Hkv, D, BF16)
+    assert err_o == 1 and err_g == 1
+    check16(q_g, q_o, BF16, "q_out")
+    _check_cache(kc_g, kc_o, BF16, "k_cache")
+    check_exact(vc_g, vc_o, "v_cache")
+
+
 def test_qkv_only_q_norm_and_out_of_range(fr):
     T, Hq, Hkv, D, P, pages = 6, 4, 2, 64, 4, 3
     announce("qkv out-of-range positions / q_norm only")
