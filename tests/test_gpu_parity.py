@@ -104,6 +104,11 @@ ADA_CASES = [
     (8192, 1024, F16, oracle.Q_STATIC, 56.0, 102),      # bandwidth config
     (8192, 1024, F16, oracle.Q_TOKEN, 0.0, 102),
     (4, 20000, BF16, oracle.Q_TOKEN, 0.0, 304),         # wide row
+    # bandwidth path (two single-wave rows per workgroup) with a ragged
+    # width and an odd token count: the last workgroup's second row is a
+    # duplicate that stores nothing
+    (2049, 1040, F16, oracle.Q_TOKEN, 0.0, 305),
+    (3001, 528, BF16, oracle.Q_STATIC, 56.0, 306),
 ]
 
 
