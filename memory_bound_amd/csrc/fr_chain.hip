@@ -7,9 +7,10 @@
 // of gate + residual + AdaRMSNorm + FP8, with QKV post-processing per layer,
 // and launch count dominates).
 //
-// Every output location of the chain belongs to one wave (or, for rows wider
-// than 512 values, one group of four waves) for the whole chain: row t's waves run
-// op (a') on token row t for every op n = s L + l in order; each further
+// Every output location of the chain belongs to one wave (or, for rows
+// wider than 512 values, one group of four waves) for the whole chain: row
+// t's waves run op (a') on token row t for every op n = s L + l in order;
+// each further
 // wave owns a fixed set of (token, head) units and runs op (b) on them for
 // every op in order.  The only value one op hands to the next is the
 // residual row, and it stays in the registers of its row waves (it is still
@@ -32,9 +33,10 @@ namespace fr {
 // Row waves: the inputs of op (a') for the next PA ops sit in a register
 // ring (slot d holds op n with n % PA == d), refilled as each op retires, so
 // only the residual hand-off is serial.  Unit waves: likewise PB ops deep.
-// FULL: every lane's CPL chunks are inside the row (H = 512 CPL), so the
-// stores need no guard and consecutive ops form one basic block the
-// compiler can interleave.
+// FULL: every lane's chunks are inside the row (H = 512 for one wave of
+// 8-value chunks, 1024 for four waves of 4-value chunks), so the stores
+// need no guard and consecutive ops form one basic block the compiler can
+// interleave.
 //
 // NWR > 1: a row is split over NWR waves (wave part p takes the 64-chunk
 // blocks NWR k + p), which divides each wave's work per op, the serial part
