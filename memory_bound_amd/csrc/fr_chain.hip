@@ -10,11 +10,10 @@
 // Every output location of the chain belongs to one wave (or, for rows
 // wider than 512 values, one group of four waves) for the whole chain: row
 // t's waves run op (a') on token row t for every op n = s L + l in order;
-// each further
-// wave owns a fixed set of (token, head) units and runs op (b) on them for
-// every op in order.  The only value one op hands to the next is the
-// residual row, and it stays in the registers of its row waves (it is still
-// stored, as each op's output).  So program order within each wave is all
+// each further wave owns a fixed set of (token, head) units and runs op (b)
+// on them for every op in order.  The only value one op hands to the next
+// is the residual row, and it stays in the registers of its row waves (it is
+// still stored, as each op's output).  So program order within each wave is all
 // the ordering the chain needs, apart from the sum of squares that a row's
 // waves exchange per op inside their own workgroup: no grid-wide
 // synchronisation (nothing can deadlock).  What remains serial is the
