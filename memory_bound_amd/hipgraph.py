@@ -38,11 +38,17 @@ class HipGraph:
         self.stream = stream
         h = _P(stream.cuda_stream)
         _ok(_hip.hipStreamBeginCapture(h, CAPTURE_MODE_RELAXED), "hipStreamBeginCapture")
+        graph = _P()
         try:
             fn()
-        finally:
-            graph = _P()
-            _ok(_hip.hipStreamEndCapture(h, ctypes.byref(graph)), "hipStreamEndCapture")
+        except BaseException:
+            # end the capture so the stream is usable again, drop the partial
+            # graph, and let the callable's own error through
+            _hip.hipStreamEndCapture(h, ctypes.byref(graph))
+            if graph:
+                _hip.hipGraphDestroy(graph)
+            raise
+        _ok(_hip.hipStreamEndCapture(h, ctypes.byref(graph)), "hipStreamEndCapture")
         self.graph = graph
         self.exec = _P()
         _ok(_hip.hipGraphInstantiate(ctypes.byref(self.exec), graph, None, None, 0),
