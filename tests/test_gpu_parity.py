@@ -198,11 +198,13 @@ def test_qkv_normrope_kvwrite(fr, case):
     check_exact(vc_g, vc_o, "v_cache")
 
 
+@pytest.mark.parametrize("T", [128, 2048], ids=["T128", "T2048_bandwidth"])
 @pytest.mark.parametrize("qs", [0.0625, 128 ** -0.5, 3.0])
-def test_qkv_q_prescale(fr, qs):
+def test_qkv_q_prescale(fr, qs, T):
     """Q pre-scale folded into RoPE (the attention's Q preparation):
-    Qwen3 prefill shape; a power of two, 1/sqrt(D) and a scale above 1."""
-    T, Hq, Hkv, D, P, pages = 128, 32, 8, 128, 16, 512
+    Qwen3 prefill shape (and the bandwidth-regime kernel at 2048 tokens); a
+    power of two, 1/sqrt(D) and a scale above 1."""
+    Hq, Hkv, D, P, pages = 32, 8, 128, 16, 512
     announce(f"qkv q_scale={qs:.6g} T={T}")
     inp = workloads.qkv_inputs(T, Hq, Hkv, D, BF16, 408, page_size=P,
                                num_pages=pages)
