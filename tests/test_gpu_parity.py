@@ -168,6 +168,8 @@ QKV_CASES = [
     # bandwidth regime, 80 heads = 10 groups of 8: the token's last wave
     # takes fewer groups than the others
     ("wide_heads_2048", 2048, 64, 8, 128, BF16, True, 1e6, 0, 16, 128, True, None, 410),
+    # the bandwidth-regime kernel with interleaved RoPE pairs, fp16, D = 64
+    ("interleaved_2048_f16", 2048, 8, 2, 64, F16, True, 1e4, 1, 16, 128, True, None, 413),
 ]
 
 
