@@ -170,6 +170,9 @@ QKV_CASES = [
     ("wide_heads_2048", 2048, 64, 8, 128, BF16, True, 1e6, 0, 16, 128, True, None, 410),
     # the bandwidth-regime kernel with interleaved RoPE pairs, fp16, D = 64
     ("interleaved_2048_f16", 2048, 8, 2, 64, F16, True, 1e4, 1, 16, 128, True, None, 413),
+    # the bandwidth-regime kernel at D = 256 (16 lanes per head) and D = 16
+    ("d256_2048", 2048, 8, 1, 256, BF16, True, 1e4, 0, 16, 128, True, None, 414),
+    ("d16_2048_interleaved", 2048, 6, 2, 16, F16, True, 1e4, 1, 16, 128, True, None, 415),
 ]
 
 
