@@ -34,6 +34,7 @@ CASES = [
     # per-head norm over four full passes of heads (one workgroup per pass),
     # 3D RoPE, interleaved pairs
     ("rms_head_3d_four_passes", 50, 64, 32, 128, BF16, 1, False, True, (22, 21, 21), 1, 1e4, 0.5, 614),
+    ("layer_head_f16_three_passes", 33, 32, 32, 128, F16, 2, False, False, None, 1, 1e4, 1.0, 615),
 ]
 
 
