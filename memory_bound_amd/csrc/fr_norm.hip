@@ -379,11 +379,20 @@ __global__ __launch_bounds__(512) void k_norm(NormArgs a) {
             const double c6 = rstd_d * a.inv6g;
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
-                double m = 0.0;
+                double m;
+                if constexpr (MODE == M_ONE_PLUS) {          // |t| = |hi + lo| needs fp64
+                    m = 0.0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    m = fmax(m, fabs((double)th[k][e] + (double)tl[k][e]));
-                m = fmax(m, dpp_d<DPP_PAIR>(m));         // the block's other lane
+                    for (int e = 0; e < 8; ++e)
+                        m = fmax(m, fabs((double)th[k][e] + (double)tl[k][e]));
+                    m = fmax(m, dpp_d<DPP_PAIR>(m));     // the block's other lane
+                } else {                                     // t is exact in fp32
+                    float mf = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) mf = fmaxf(mf, fabsf(th[k][e]));
+                    mf = group_reduce<2>(mf, OpMaxMag());    // the block's other lane
+                    m = (double)mf;
+                }
                 const double sd = m * c6;
                 const float sh = (float)sd;
                 const float sf = round_odd(sh, (float)(sd - (double)sh));
